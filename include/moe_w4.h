@@ -1,0 +1,216 @@
+/*
+ * moe_w4.h - C ABI of the MI355X (gfx950) sparse MoE expert layer with fused
+ * groupwise-affine 4-bit weight reconstruction.
+ *
+ * Sources (web pages on the Lily engine for Qwen3.6-35B-A3B):
+ *   [LB] "Lily Beats MLX-LM 1.35x on Decode: Perplexity's Rust+Metal Engine for
+ *        Apple Silicon": "Model structure and three workload shapes" (router
+ *        over 256 experts, eight selected, one shared expert for every token;
+ *        4-bit codes, a bfloat16 scale and bias per group of 64 weights,
+ *        weights reconstructed to bfloat16 for the tensor operations) and
+ *        "Prefill: fusing dequantisation and keeping routing GPU-resident"
+ *        (reconstruction one tile at a time inside the grouped GEMM with float32
+ *        accumulation, the expanded array never written to memory; histogram,
+ *        prefix scan, scatter and block map on the GPU with no CPU
+ *        synchronisation; 32-row tiles; bounded chunks for long prompts).
+ *   [RL] "Introduction: Revolutionizing Local AI Inference on Apple Silicon":
+ *        "Understanding the Qwen3.6-35B-A3B Model", "Optimizing Prefill
+ *        Operations" (the same routing stages and the fused dequantisation).
+ *
+ * Conventions shared by every call:
+ *   - All array arguments are DEVICE pointers to memory the caller allocated and
+ *     owns; the library never allocates, frees or synchronises, and keeps no
+ *     state between calls apart from a per-device architecture check.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously in call order; the caller synchronises.
+ *   - bfloat16 values are passed as uint16_t bit patterns.
+ *   - Every argument is validated before anything is enqueued, so an error
+ *     return leaves nothing half-launched.  T = 0 is valid and enqueues nothing.
+ *   - Faults found on the device (a NaN router score, an out-of-range index in
+ *     the routing tables) set bits in out->status, which the caller reads after
+ *     its own synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_W4_ABI_VERSION 1
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)  /* null required pointer or a dimension out of range   */
+#define MOE_EALIGN (-2)  /* a pointer is not aligned as documented              */
+#define MOE_EWS (-3)     /* workspace smaller than moe_route_ws_bytes()        */
+#define MOE_EDEVICE (-4) /* current device is not gfx950, or a HIP query failed */
+#define MOE_ELAUNCH (-5) /* a kernel launch reported an error                   */
+
+/* Bits of the device status word. */
+#define MOE_STATUS_NAN_LOGIT 1u   /* a router score was NaN (treated as -inf)           */
+#define MOE_STATUS_BAD_INDEX 2u   /* a routing table entry was out of range (skipped)   */
+#define MOE_STATUS_BLOCK_OVERFLOW 4u /* block map longer than moe_max_blocks (truncated) */
+
+/*
+ * Layer dimensions.
+ *   T          tokens in this call (one chunk of a long prompt), 0 <= T <= 2^20
+ *   H          hidden size, a positive multiple of 64
+ *   I          expert intermediate size, a positive multiple of 64
+ *   E          routed experts, 1..1024
+ *   k          experts selected per token, 1..min(E, 32)
+ *   n_shared   always-on shared experts, 0 or 1 (same shape as a routed expert)
+ *   tile_m_max largest GEMM tile height, a multiple of tile_gran in 16..256
+ *   tile_gran  tile height granularity, 16 or 32
+ * A slot is (token t, rank j < k) with id t*k + j.  The grouped GEMMs work on
+ * Rows = T*k + n_shared*T rows: the routed slots in expert order, then one
+ * shared-expert row per token in token order.
+ */
+typedef struct moe_dims {
+  int32_t T, H, I, E, k, n_shared;
+  int32_t tile_m_max, tile_gran;
+} moe_dims;
+
+/*
+ * One bank of n experts in the packed groupwise-affine 4-bit layout [LB, "Model
+ * structure ..."].  Each matrix is [n][rows][K] with rows = output features and
+ * K = input features; every row is cut into groups of 64 consecutive inputs
+ * that share one bfloat16 scale and one bfloat16 bias.  Byte b of a row holds
+ * input 2b in its low nibble and 2b+1 in its high nibble; codes q are unsigned
+ * 0..15 and the weight is w = bf16(fma(q, scale, bias)) (float32 fused
+ * multiply-add, rounded once to nearest-even bfloat16).
+ *   gu_q [n][2I][H/2] uint8   gate rows 0..I-1, up rows I..2I-1   (16-byte aligned)
+ *   gu_s, gu_b [n][2I][H/64] bfloat16                               (4-byte aligned)
+ *   dn_q [n][H][I/2] uint8                                          (16-byte aligned)
+ *   dn_s, dn_b [n][H][I/64] bfloat16                                (4-byte aligned)
+ */
+typedef struct moe_w4_bank {
+  const uint8_t *gu_q;
+  const uint16_t *gu_s, *gu_b;
+  const uint8_t *dn_q;
+  const uint16_t *dn_s, *dn_b;
+} moe_w4_bank;
+
+/*
+ * Routing tables written by moe_route and read by the later calls.  All are
+ * device arrays owned by the caller (4-byte aligned unless stated).
+ *   topk_idx [T][k] int32   selected experts, best first (higher score first,
+ *                           equal scores by lower expert index)
+ *   topk_w   [T][k] float   softmax over all E scores, restricted to the
+ *                           selected experts and renormalised to sum to one
+ *   counts   [E]    int32   slots routed to each expert (the histogram)
+ *   offsets  [E+1]  int32   exclusive prefix sum of counts; offsets[E] = T*k
+ *   sorted_slot [T*k] int32 slot ids in expert order, stable in slot-id order
+ *   slot_pos [T*k]  int32   inverse permutation: row of each slot
+ *   blocks [moe_max_blocks][4] int32  {group, first row, rows, tile height}:
+ *                           groups are experts 0..E-1 then the shared expert
+ *                           E; a group of c rows is cut into ceil(c/tile_m_max)
+ *                           blocks whose sizes differ by at most one, tile
+ *                           height = ceil(c/nb) rounded up to tile_gran
+ *   n_blocks [1] int32      entries written to blocks
+ *   logits [T][E] float or NULL: exported router scores (diagnostic)
+ *   status [1] uint32       device error word (MOE_STATUS_*); moe_route clears
+ *                           it, later calls on the stream only set bits
+ *   ws, ws_bytes            scratch of at least moe_route_ws_bytes() bytes,
+ *                           16-byte aligned, used by moe_route only
+ */
+typedef struct moe_route_out {
+  int32_t *topk_idx;
+  float *topk_w;
+  int32_t *counts, *offsets;
+  int32_t *sorted_slot, *slot_pos;
+  int32_t *blocks, *n_blocks;
+  float *logits;
+  uint32_t *status;
+  void *ws;
+  size_t ws_bytes;
+} moe_route_out;
+
+/* MOE_W4_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Static text for a return code. */
+const char *moe_strerror(int code);
+
+/* Upper bound on the block map length for d:
+ * floor(T*k / tile_m_max) + min(E, T*k) + n_shared * ceil(T / tile_m_max).
+ * Returns -1 if d is invalid. */
+int32_t moe_max_blocks(const moe_dims *d);
+
+/* Scratch bytes moe_route needs for d (0 if d is invalid). */
+size_t moe_route_ws_bytes(const moe_dims *d);
+
+/*
+ * moe_route - router scores, top-k, weights, histogram, prefix scan, scatter and
+ * block map, all on the GPU and enqueued with no host synchronisation
+ * [LB, "Prefill: ..."], [RL, "Optimizing Prefill Operations"].
+ *   x          [T][H] bfloat16 token activations (16-byte aligned)
+ *   w_router   [H][E] float32 router weights (row h = weights of input h)
+ *   logit_bias [E] float32 added to every token's scores, or NULL
+ * Scores are float32 in a fixed order: partial m (0..63) is a fused
+ * multiply-add chain from +0 over inputs h = m, m+64, ... in increasing h;
+ * the partials are added as a tree (for s = 32..1: p[i] += p[i+s], i < s);
+ * then the bias is added.  This makes the selection reproducible bit for bit.
+ */
+int moe_route(const moe_dims *d, const uint16_t *x, const float *w_router, const float *logit_bias,
+              const moe_route_out *out, void *stream);
+
+/*
+ * moe_w4_gate_up - grouped gate/up GEMM with the 4-bit weights reconstructed
+ * tile by tile inside the kernel (never written out), float32 accumulation and
+ * SwiGLU in the epilogue [LB, "Prefill: ..."].  For every block of the map:
+ * h[row] = silu(g) * u, g = W_gate x_t, u = W_up x_t, rounded to bfloat16,
+ * where t is the row's token (sorted_slot[row] / k for routed rows,
+ * row - T*k for shared rows).
+ *   x        [T][H] bfloat16, the same activations given to moe_route
+ *   r        tables from moe_route (blocks, n_blocks, sorted_slot, status)
+ *   routed   bank of E experts;  shared  bank of 1 expert or NULL if n_shared = 0
+ *   h        [Rows][I] bfloat16 output (16-byte aligned)
+ */
+int moe_w4_gate_up(const moe_dims *d, const uint16_t *x, const moe_route_out *r,
+                   const moe_w4_bank *routed, const moe_w4_bank *shared, uint16_t *h,
+                   void *stream);
+
+/*
+ * moe_w4_down - grouped down GEMM with fused reconstruction:
+ * y_slots[row] = W_down h[row], float32 accumulation, rounded to bfloat16.
+ *   h        [Rows][I] bfloat16 from moe_w4_gate_up (16-byte aligned)
+ *   y_slots  [Rows][H] bfloat16 output (16-byte aligned)
+ */
+int moe_w4_down(const moe_dims *d, const moe_route_out *r, const moe_w4_bank *routed,
+                const moe_w4_bank *shared, const uint16_t *h, uint16_t *y_slots, void *stream);
+
+/* moe_grouped_w4_ffn - moe_w4_gate_up followed by moe_w4_down on one stream. */
+int moe_grouped_w4_ffn(const moe_dims *d, const uint16_t *x, const moe_route_out *r,
+                       const moe_w4_bank *routed, const moe_w4_bank *shared, uint16_t *h,
+                       uint16_t *y_slots, void *stream);
+
+/*
+ * moe_combine - weighted top-k combine [RL, "Understanding the Qwen3.6-35B-A3B
+ * Model"]: y[t] = sum_j topk_w[t][j] * y_slots[slot_pos[t*k+j]]
+ * (+ y_slots[T*k + t] when n_shared = 1), float32, j ascending, shared last,
+ * rounded to bfloat16.
+ *   y_slots [Rows][H] bfloat16;  y [T][H] bfloat16 output (both 16-byte aligned)
+ */
+int moe_combine(const moe_dims *d, const moe_route_out *r, const uint16_t *y_slots, uint16_t *y,
+                void *stream);
+
+/*
+ * moe_w4_dequant - expand a packed [rows][K] matrix to bfloat16 in memory, with
+ * the same device reconstruction the GEMMs use.  Diagnostic: it materialises
+ * exactly the array the fused GEMMs avoid, for bit-exactness checks and for the
+ * unfused comparison [LB, "Prefill: ..."].
+ *   q [rows][K/2] (16-byte aligned), s, b [rows][K/64], out [rows][K] (16-byte aligned)
+ *   K a positive multiple of 64, rows >= 0.
+ */
+int moe_w4_dequant(int32_t rows, int32_t K, const uint8_t *q, const uint16_t *s, const uint16_t *b,
+                   uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4_H */

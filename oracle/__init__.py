@@ -21,4 +21,5 @@ from .api import (  # noqa: F401
     moe_layer,
     route,
     relative_error,
+    relative_error_elementwise,
 )

@@ -1,0 +1,108 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and rejects bad arguments with the documented codes before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4_dequant_expert_amd as moe
+from w4_dequant_expert_amd.moe import Bank, Dims, RouteOut
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_w4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "moe_route" in names and "moe_combine" in names and "moe_grouped_w4_ffn" in names
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(moe.EXPORTED) == names
+
+
+def test_version_and_strerror():
+    assert moe.moe_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert moe.strerror(code) and moe.strerror(code) != "unknown error"
+
+
+def full(T=512):
+    return moe.make_dims(T, 2048, 512, 256, 8, 1, 128, 16)
+
+
+def test_max_blocks_and_workspace():
+    import oracle
+    for T in (0, 1, 16, 512, 2048):
+        d = full(T)
+        assert moe.moe_max_blocks(d) == oracle.max_blocks(T, 256, 8, 1, 128)
+    d = full(2048)
+    assert moe.moe_route_ws_bytes(d) >= 2048 * 256 * 4 + 2048 * 8 * 4
+    assert moe.moe_max_blocks(moe.make_dims(4, 64, 64, 8, 9, 0)) == -1      # k > E
+    assert moe.moe_route_ws_bytes(moe.make_dims(4, 100, 64, 8, 2, 0)) == 0  # H % 64
+
+
+@pytest.mark.parametrize("field,value", [("H", 96), ("I", 0), ("E", 0), ("E", 2000), ("k", 0),
+                                         ("k", 33), ("n_shared", 2), ("tile_m_max", 24),
+                                         ("tile_m_max", 512), ("tile_gran", 8), ("T", -1)])
+def test_invalid_dims_rejected(field, value):
+    d = full(4)
+    setattr(d, field, value)
+    assert moe.moe_max_blocks(d) == -1
+    out = RouteOut(*([0x1000] * 11), 1 << 30)
+    rc = moe.lib().moe_route(ctypes.byref(d), 0x1000, 0x1000, None, ctypes.byref(out), None)
+    assert rc == moe.moe.MOE_EINVAL
+
+
+def _route_out(ws_bytes=1 << 30, base=0x10000):
+    return RouteOut(*[base + 256 * i for i in range(11)], ws_bytes)
+
+
+def test_route_validation_codes():
+    L = moe.lib()
+    d = full(4)
+    out = _route_out()
+    assert L.moe_route(ctypes.byref(d), None, 0x1000, None, ctypes.byref(out), None) == -1
+    assert L.moe_route(ctypes.byref(d), 0x1008, 0x1000, None, ctypes.byref(out), None) == -2
+    assert L.moe_route(ctypes.byref(d), 0x1000, 0x1002, None, ctypes.byref(out), None) == -2
+    small = _route_out(ws_bytes=16)
+    assert L.moe_route(ctypes.byref(d), 0x1000, 0x1000, None, ctypes.byref(small), None) == -3
+    bad = _route_out()
+    bad.blocks = 0x10004                     # block map needs 16-byte alignment
+    assert L.moe_route(ctypes.byref(d), 0x1000, 0x1000, None, ctypes.byref(bad), None) == -2
+    nul = _route_out()
+    nul.status = None
+    assert L.moe_route(ctypes.byref(d), 0x1000, 0x1000, None, ctypes.byref(nul), None) == -1
+    # T = 0 is a valid no-op and touches nothing
+    d0 = full(0)
+    assert L.moe_route(ctypes.byref(d0), 0x1000, 0x1000, None, ctypes.byref(out), None) == 0
+
+
+def test_ffn_and_combine_validation_codes():
+    L = moe.lib()
+    d = full(4)
+    out = _route_out()
+    bank = Bank(0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000)
+    assert L.moe_w4_gate_up(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                            None, 0x8000, None) == -1          # shared bank missing
+    mis = Bank(0x2008, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000)
+    assert L.moe_w4_gate_up(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(mis),
+                            ctypes.byref(bank), 0x8000, None) == -2
+    assert L.moe_w4_down(ctypes.byref(d), ctypes.byref(out), ctypes.byref(bank),
+                         ctypes.byref(bank), 0x8000, 0x9004, None) == -2
+    assert L.moe_grouped_w4_ffn(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                                ctypes.byref(bank), 0x8000, None, None) == -1
+    assert L.moe_combine(ctypes.byref(d), ctypes.byref(out), 0x1000, 0x1001, None) == -2
+    d0 = full(0)
+    assert L.moe_grouped_w4_ffn(ctypes.byref(d0), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                                ctypes.byref(bank), 0x8000, 0x9000, None) == 0
+    assert L.moe_w4_dequant(4, 100, 0x1000, 0x2000, 0x3000, 0x4000, None) == -1
+    assert L.moe_w4_dequant(0, 64, 0x1000, 0x2000, 0x3000, 0x4000, None) == 0

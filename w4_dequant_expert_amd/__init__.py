@@ -1,0 +1,34 @@
+"""MI355X (gfx950) sparse MoE expert layer with fused groupwise-affine 4-bit weights.
+
+The compute lives in libmoe_w4.so (hand-written HIP, C ABI in include/moe_w4.h);
+this package only marshals arguments to it.
+"""
+
+from .moe import (  # noqa: F401
+    Bank,
+    DeviceBank,
+    Dims,
+    EXPORTED,
+    LIB_PATH,
+    MoeError,
+    MoeLayer,
+    RouteOut,
+    RouteTables,
+    STATUS_BAD_INDEX,
+    STATUS_BLOCK_OVERFLOW,
+    STATUS_NAN_LOGIT,
+    lib,
+    make_dims,
+    moe_abi_version,
+    moe_combine,
+    moe_grouped_w4_ffn,
+    moe_max_blocks,
+    moe_route,
+    moe_route_ws_bytes,
+    moe_w4_dequant,
+    moe_w4_down,
+    moe_w4_gate_up,
+    strerror,
+)
+
+lib()  # load the HIP library now: a missing build is an import error, never a fallback

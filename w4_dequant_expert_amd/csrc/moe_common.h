@@ -1,0 +1,77 @@
+// Device helpers shared by the gfx950 kernels of the W4 MoE expert layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_w4.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two float32 -> packed bfloat16 pair (low half = a), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float a) {
+  return static_cast<uint16_t>(pack_bf16x2(a, 0.0f) & 0xFFFFu);
+}
+
+// Reconstruct eight consecutive 4-bit weights of one row (one 32-bit word of
+// packed codes, element i in bits 4i..4i+3) that share one group's scale s and
+// bias b: w_i = bf16(fma(q_i, s, b)).  Returns the eight bfloat16 values in
+// element order, packed two per 32-bit word (element 2p in the low half).
+//   - even elements sit in the low nibble of each byte, odd ones in the high
+//     nibble; masking gives one code per byte, v_cvt_f32_ubyteN widens it
+//     exactly;
+//   - one float32 fused multiply-add per weight, then one round to bfloat16.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b) {
+  const uint32_t ev = w & 0x0F0F0F0Fu;          // codes 0,2,4,6
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // codes 1,3,5,7
+  float f0 = __builtin_fmaf(static_cast<float>(ev & 0xFFu), s, b);
+  float f1 = __builtin_fmaf(static_cast<float>(od & 0xFFu), s, b);
+  float f2 = __builtin_fmaf(static_cast<float>((ev >> 8) & 0xFFu), s, b);
+  float f3 = __builtin_fmaf(static_cast<float>((od >> 8) & 0xFFu), s, b);
+  float f4 = __builtin_fmaf(static_cast<float>((ev >> 16) & 0xFFu), s, b);
+  float f5 = __builtin_fmaf(static_cast<float>((od >> 16) & 0xFFu), s, b);
+  float f6 = __builtin_fmaf(static_cast<float>(ev >> 24), s, b);
+  float f7 = __builtin_fmaf(static_cast<float>(od >> 24), s, b);
+  uint4 r;
+  r.x = pack_bf16x2(f0, f1);
+  r.y = pack_bf16x2(f2, f3);
+  r.z = pack_bf16x2(f4, f5);
+  r.w = pack_bf16x2(f6, f7);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ void status_set(uint32_t* status, uint32_t bits) {
+  if (status) atomicOr(status, bits);
+}
+
+// Pointers of one expert bank (device) as seen by the kernels.
+struct BankView {
+  const uint8_t* gu_q;
+  const uint16_t* gu_s;
+  const uint16_t* gu_b;
+  const uint8_t* dn_q;
+  const uint16_t* dn_s;
+  const uint16_t* dn_b;
+};
+
+}  // namespace moe

@@ -1,0 +1,54 @@
+// Internal launch interface of the routing, GEMM and combine kernels.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+// Tokens per top-k workgroup: its slots (tokens * k) fit one 256-lane workgroup.
+inline int route_tokens_per_wg(int k) { return 256 / k; }
+
+struct RouteBuffers {
+  float* logits;         // [T][E]
+  int32_t* topk_idx;     // [T][k]
+  float* topk_w;         // [T][k]
+  int32_t* counts;       // [E]
+  int32_t* offsets;      // [E+1]
+  int32_t* sorted_slot;  // [T*k]
+  int32_t* slot_pos;     // [T*k]
+  int32_t* blocks;       // [max_blocks][4]
+  int32_t* n_blocks;     // [1]
+  int32_t* partial;      // [n_route_wg][E]   (workspace)
+  int32_t* local_rank;   // [T*k]             (workspace)
+  uint32_t* status;
+  int max_blocks;
+};
+
+hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, const float* bias,
+                        const RouteBuffers& rb, hipStream_t stream);
+
+struct GemmArgs {
+  int T, H, I, E, k, n_shared, max_blocks;
+  const int32_t* blocks;
+  const int32_t* n_blocks;
+  const int32_t* sorted_slot;
+  BankView routed, shared;
+  uint32_t* status;
+};
+
+// M_MAX: largest tile height the chosen kernel variant accepts (64, 128, 256).
+int gemm_m_max_for(int tile_m_max);
+hipError_t launch_gate_up(const GemmArgs& a, int m_max, const uint16_t* x, uint16_t* h,
+                          hipStream_t stream);
+hipError_t launch_down(const GemmArgs& a, int m_max, const uint16_t* h, uint16_t* y_slots,
+                       hipStream_t stream);
+hipError_t launch_combine(int T, int H, int k, int n_shared, const float* topk_w,
+                          const int32_t* slot_pos, const uint16_t* y_slots, uint16_t* y,
+                          uint32_t* status, hipStream_t stream);
+hipError_t launch_dequant(int rows, int K, const uint8_t* q, const uint16_t* s, const uint16_t* b,
+                          uint16_t* out, hipStream_t stream);
+
+}  // namespace moe
