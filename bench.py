@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X W4 MoE expert layer.
+
+One step = one pass of the whole hot path over one batch of T tokens:
+moe_route -> moe_w4_gate_up -> moe_w4_down -> moe_combine, on the
+prefill workload of 512 tokens (hidden 2048, 256 routed experts top-8 plus one
+shared expert, expert intermediate 512, 4-bit weights in groups of 64).
+Inputs are resident in HBM before timing starts; R copies of the weights (and
+router) are rotated so that no call finds the previous call's weights in the
+256 MB Infinity Cache.
+
+Prints one JSON line.  Also measured (reported under "extra"): the
+2048-token Zipf-skewed prefill (MFMA fraction of the two GEMMs) and batch-1
+decode (HBM fraction of the two GEMMs), and the CPU oracle on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_prefill512.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--copies", type=int, default=4, help="weight copies rotated between steps")
+    p.add_argument("--tile-m-max", type=int, default=128)
+    p.add_argument("--no-extra", action="store_true", help="skip the 2048-token and decode legs")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--calib-copy-mb", type=int, default=0,
+                   help="also run one plain device copy of this size (counter calibration)")
+    p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1"], default=None,
+                   help="time a single workload (profiling runs)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("moe_common.h", "route.h", "ffn.hip"):
+        with open(os.path.join(ROOT, "w4_dequant_expert_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """Device-resident inputs of one configuration and R rotated weight copies."""
+
+    def __init__(self, name, copies, tile_m_max, T=None):
+        import numpy as np
+        import torch
+
+        import w4_dequant_expert_amd as moe
+        from synth import build_config
+
+        c = build_config(name, T=T)
+        sh = c["shape"]
+        self.name, self.c, self.sh = name, c, sh
+        self.T = c["T"]
+        base_r = moe.DeviceBank(c["routed"])
+        base_s = moe.DeviceBank(c["shared"])
+        wr = torch.from_numpy(c["wr"]).to("cuda")
+        bias = None if c["bias"] is None else torch.from_numpy(c["bias"]).to("cuda")
+        self.copies = [(base_r, base_s, wr)]
+        for _ in range(copies - 1):
+            self.copies.append((base_r.clone(), base_s.clone(), wr.clone()))
+        self.layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, base_r, base_s, wr, bias,
+                                  T_max=max(self.T, 1), tile_m_max=tile_m_max, export_logits=False)
+        self.x = torch.from_numpy(c["x"].view(np.int16)).to("cuda")
+        self.y = torch.empty((self.T, sh.H), dtype=torch.int16, device="cuda")
+
+    def step(self, i, ev=None, x=None):
+        r, s, wr = self.copies[i % len(self.copies)]
+        L = self.layer
+        L.w_router = wr
+        x = self.x if x is None else x
+        if ev is not None:
+            ev[0].record()
+        d = L.route(x)
+        if ev is not None:
+            ev[1].record()
+        L.gate_up(d, x, r, s)
+        if ev is not None:
+            ev[2].record()
+        L.down(d, r, s)
+        if ev is not None:
+            ev[3].record()
+        L.combine(d, self.y)
+        if ev is not None:
+            ev[4].record()
+
+    def work(self):
+        """Algorithmic flops and bytes of one call, from the real routing counts."""
+        import torch
+        torch.cuda.synchronize()
+        counts = self.layer.rt.counts.cpu().numpy()
+        sh, T = self.sh, self.T
+        H, I, E, k = sh.H, sh.I, sh.E, sh.k
+        rows = T * k + (T if sh.n_shared else 0)
+        touched = int((counts > 0).sum()) + sh.n_shared
+        gu_w = 2 * I * H * 9 // 16           # 4.5 bits per weight
+        dn_w = H * I * 9 // 16
+        return dict(
+            rows=rows, touched=touched,
+            flops_gate_up=rows * 4 * H * I, flops_down=rows * 2 * H * I,
+            bytes_gate_up=touched * gu_w + T * H * 2 + rows * I * 2,
+            bytes_down=touched * dn_w + rows * I * 2 + rows * H * 2,
+            bytes_layer=touched * (gu_w + dn_w) + H * E * 4 + 2 * T * H * 2,
+        )
+
+
+def time_workload(wl, steps, warmup, fresh_tokens=None):
+    """Wall time of `steps` steps and per-stage HIP event durations (ms)."""
+    import torch
+    for i in range(warmup):
+        wl.step(i, x=None if fresh_tokens is None else fresh_tokens[i % len(fresh_tokens)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(warmup + i, evs[i],
+                x=None if fresh_tokens is None else fresh_tokens[(warmup + i) % len(fresh_tokens)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = [0.0] * 4
+    for e in evs:
+        for j in range(4):
+            stage[j] += e[j].elapsed_time(e[j + 1])
+    stage = [s / steps for s in stage]
+    return wall, dict(route_ms=stage[0], gate_up_ms=stage[1], down_ms=stage[2], combine_ms=stage[3])
+
+
+def traffic_record():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None       # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(name, budget_tokens):
+    """The oracle, untuned, on the host cores: route + layer for a sample of the batch."""
+    import oracle
+    from synth import build_config
+    c = build_config(name, T=budget_tokens)
+    sh = c["shape"]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    r = oracle.route(c["x"], c["wr"], c["bias"], sh.k, sh.n_shared, 128, 16, nthreads=threads)
+    oracle.moe_layer(c["x"], r["topk_idx"], r["topk_w"], c["routed"], c["shared"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=budget_tokens / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"first {budget_tokens} tokens of the {name} batch: router, top-k, tables and "
+                       f"float64 layer output ({dt:.1f} s)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the layer shards by token with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import w4_dequant_expert_amd  # noqa: F401  (fails loudly without the HIP library)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n}), file=sys.stderr)
+        del a, b
+
+    extra = {}
+    main_name = args.only or "prefill512"
+    wl = Workload(main_name, args.copies, args.tile_m_max)
+    fresh = None
+    if main_name == "decode1":
+        from synth import make_tokens
+        fresh = [torch.from_numpy(make_tokens(1, 2048, 4, t0=i).view(np.int16)).to("cuda")
+                 for i in range(256)]
+    wall, stages = time_workload(wl, args.steps, args.warmup, fresh)
+    work = wl.work()
+    ms = wall / args.steps * 1e3
+    tok_s = wl.T * args.steps / wall
+    gu_s = stages["gate_up_ms"] * 1e-3
+    dn_s = stages["down_ms"] * 1e-3
+    achieved = work["bytes_gate_up"] / gu_s / 1e9
+    gemm_tflops = (work["flops_gate_up"] + work["flops_down"]) / (gu_s + dn_s) / 1e12
+    gemm_gbs = (work["bytes_gate_up"] + work["bytes_down"]) / (gu_s + dn_s) / 1e9
+    extra[main_name] = dict(
+        tokens_per_s=tok_s, ms_per_step=ms, **{k: round(v, 5) for k, v in stages.items()},
+        gemm_tflops=gemm_tflops, gemm_frac_mfma=gemm_tflops / PEAK_BF16_TFLOPS,
+        gemm_hbm_gbs=gemm_gbs, gemm_frac_hbm=gemm_gbs / PEAK_HBM_GBS,
+        layer_bytes=work["bytes_layer"], touched_experts=work["touched"])
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_extra and args.only is None:
+        wl2 = Workload("prefill2048_zipf", args.copies, args.tile_m_max)
+        w2, st2 = time_workload(wl2, max(args.steps // 2, 5), max(args.warmup // 2, 3))
+        wk2 = wl2.work()
+        g2 = (st2["gate_up_ms"] + st2["down_ms"]) * 1e-3
+        extra["prefill2048_zipf"] = dict(
+            tokens_per_s=wl2.T * max(args.steps // 2, 5) / w2, **{k: round(v, 5) for k, v in st2.items()},
+            gemm_tflops=(wk2["flops_gate_up"] + wk2["flops_down"]) / g2 / 1e12,
+            gemm_frac_mfma=(wk2["flops_gate_up"] + wk2["flops_down"]) / g2 / 1e12 / PEAK_BF16_TFLOPS,
+            touched_experts=wk2["touched"])
+        del wl2
+        torch.cuda.empty_cache()
+        wl5 = Workload("decode1", 40, args.tile_m_max)
+        from synth import make_tokens
+        fresh = [torch.from_numpy(make_tokens(1, 2048, 4, t0=i).view(np.int16)).to("cuda")
+                 for i in range(200)]
+        w5, st5 = time_workload(wl5, 200, 20, fresh)
+        wk5 = wl5.work()
+        g5 = (st5["gate_up_ms"] + st5["down_ms"]) * 1e-3
+        extra["decode1"] = dict(
+            tokens_per_s=200 / w5, **{k: round(v, 5) for k, v in st5.items()},
+            gemm_hbm_gbs=(wk5["bytes_gate_up"] + wk5["bytes_down"]) / g5 / 1e9,
+            gemm_frac_hbm=(wk5["bytes_gate_up"] + wk5["bytes_down"]) / g5 / 1e9 / PEAK_HBM_GBS,
+            bytes_per_token=wk5["bytes_layer"], weight_copies=40)
+        del wl5
+        torch.cuda.empty_cache()
+
+    out = {
+        "metric": "MoE-layer tokens/s + %MFMA peak at T=512/2048; %HBM peak at T=1",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": main_name, "tokens": wl_T(main_name), "hidden": 2048,
+                   "experts": 256, "top_k": 8, "shared_experts": 1, "expert_intermediate": 512,
+                   "weights": "4-bit codes, bf16 scale+bias per 64", "weight_copies": args.copies,
+                   "tile_m_max": args.tile_m_max},
+        "roofline": {"bound": "hbm", "kernel": "w4_grouped_gemm_kernel<gate_up>",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(),
+                     "algorithmic_bytes": work["bytes_gate_up"],
+                     "avg_launch_ms": stages["gate_up_ms"]},
+        "cpu_baseline": None,
+        "extra": extra,
+    }
+    if not args.no_cpu and args.only is None:
+        out["cpu_baseline"] = cpu_baseline("prefill512", 512)
+    print(json.dumps(out))
+
+
+def wl_T(name):
+    from synth import CONFIGS
+    return CONFIGS[name]["T"]
+
+
+if __name__ == "__main__":
+    main()
