@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_prefill512.json")
+# Tile height bound per workload: uniform routing at 512 tokens gives every
+# expert 7-27 rows, so 32-row tiles cover them and the shared expert's 512
+# rows in 16 blocks; the skewed 2048-token batch has groups of up to ~2000
+# rows that want tall tiles; batch-1 decode has one row per group.
+TILE_M_MAX = {"prefill512": 32, "prefill2048_zipf": 128, "chunked16384": 128, "decode1": 32}
 
 
 def parse():
@@ -37,7 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--copies", type=int, default=4, help="weight copies rotated between steps")
-    p.add_argument("--tile-m-max", type=int, default=128)
+    p.add_argument("--tile-m-max", type=int, default=None,
+                   help="largest GEMM tile height (default: per workload)")
     p.add_argument("--no-extra", action="store_true", help="skip the 2048-token and decode legs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--calib-copy-mb", type=int, default=0,
@@ -58,7 +64,7 @@ def kernel_source_hash() -> str:
 class Workload:
     """Device-resident inputs of one configuration and R rotated weight copies."""
 
-    def __init__(self, name, copies, tile_m_max, T=None):
+    def __init__(self, name, copies, tile_m_max=None, T=None):
         import numpy as np
         import torch
 
@@ -67,6 +73,8 @@ class Workload:
 
         c = build_config(name, T=T)
         sh = c["shape"]
+        tile_m_max = tile_m_max or TILE_M_MAX[name]
+        self.tile_m_max = tile_m_max
         self.name, self.c, self.sh = name, c, sh
         self.T = c["T"]
         base_r = moe.DeviceBank(c["routed"])
@@ -258,7 +266,7 @@ def main():
         "config": {"workload": main_name, "tokens": wl_T(main_name), "hidden": 2048,
                    "experts": 256, "top_k": 8, "shared_experts": 1, "expert_intermediate": 512,
                    "weights": "4-bit codes, bf16 scale+bias per 64", "weight_copies": args.copies,
-                   "tile_m_max": args.tile_m_max},
+                   "tile_m_max": args.tile_m_max or TILE_M_MAX[main_name]},
         "roofline": {"bound": "hbm", "kernel": "w4_grouped_gemm_kernel<gate_up>",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(),

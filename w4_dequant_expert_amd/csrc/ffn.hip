@@ -29,13 +29,23 @@ namespace moe {
 
 constexpr int kKS = 128;          // reduction inputs per step
 constexpr int kLDA = kKS + 8;     // LDS row pitch in bf16 (16-byte pad against bank conflicts)
+constexpr int kSmallM = 32;       // tiles up to this height go to the small-tile kernel
+
+// Raw operands of one reduction step for one wave: 16 bytes of codes (32
+// inputs) and the group's scale and bias, for each of the wave's four
+// 16-row weight slices.
+struct CodeSlot {
+  uint4 q[4];
+  uint32_t s[4], b[4];
+};
 
 template <int M_MAX, bool GATE_UP>
-__global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(GemmArgs a,
-                                                              const uint16_t* __restrict__ src,
-                                                              uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[M_MAX * kLDA];
+__global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  // A tile of the block, double-buffered over reduction steps
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][M_MAX * kLDA];
   __shared__ int s_tok[M_MAX];
+  constexpr int AV = M_MAX / 16;  // 16-byte A chunks staged per thread per step
 
   const int T = a.T, k = a.k;
   const int Sk = T * k;
@@ -48,6 +58,7 @@ __global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(GemmArgs a,
 
   const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
   const int G = blk.x, row0 = blk.y, rows = blk.z, tm = blk.w;
+  if (tm <= kSmallM) return;  // a short block: the small-tile kernel owns it
   if (G < 0 || G >= a.E + (a.n_shared ? 1 : 0) || rows < 1 || rows > tm || tm > M_MAX ||
       (tm & 15) || row0 < 0 || row0 + rows > Rows) {
     if (threadIdx.x == 0) status_set(a.status, MOE_STATUS_BAD_INDEX);
@@ -63,17 +74,23 @@ __global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(GemmArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col0 = GATE_UP ? nt * 128 + wave * 32 : nt * 256 + wave * 64;
   const bool active = col0 < (GATE_UP ? a.I : a.H);
-  int wrow[4];
+  const uint8_t* qrow[4];
+  const uint16_t* srow[4];
+  const uint16_t* brow[4];
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
+    int wr;
     if (GATE_UP)
-      wrow[ns] = (ns < 2 ? col0 + ns * 16 : a.I + col0 + (ns - 2) * 16) + (lane & 15);
+      wr = (ns < 2 ? col0 + ns * 16 : a.I + col0 + (ns - 2) * 16) + (lane & 15);
     else
-      wrow[ns] = col0 + ns * 16 + (lane & 15);
+      wr = col0 + ns * 16 + (lane & 15);
+    if (!active) wr = 0;
+    qrow[ns] = Q + static_cast<size_t>(wr) * (K / 2);
+    srow[ns] = Sc + static_cast<size_t>(wr) * (K / 64);
+    brow[ns] = Bi + static_cast<size_t>(wr) * (K / 64);
   }
 
-  // token of every tile row (gate/up) ; -1 pads the tile
-  if (GATE_UP) {
+  if (GATE_UP) {  // token of every tile row; -1 pads the tile
     for (int m = tid; m < tm; m += 256) {
       int tok = -1;
       if (m < rows) {
@@ -86,22 +103,32 @@ __global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(GemmArgs a,
       }
       s_tok[m] = tok;
     }
+    __syncthreads();
   }
 
+  const int nk = (K + kKS - 1) / kKS;
   const int mtiles = tm >> 4;
-  f32x4 acc[M_MAX / 16][4];
-#pragma unroll
-  for (int mt = 0; mt < M_MAX / 16; ++mt)
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int lk = (lane >> 4) * 32;  // this lane's 32 inputs within a step
 
-  for (int kb = 0; kb < K; kb += kKS) {
-    __syncthreads();
-    for (int idx = tid; idx < tm * (kKS / 8); idx += 256) {
-      const int m = idx / (kKS / 8), c = idx % (kKS / 8);
-      const int kk = kb + c * 8;
+  // ---- operand movers ----------------------------------------------------
+  auto load_codes = [&](int s, CodeSlot& cs) {
+    const int kl = s * kKS + lk;
+    if (!active || s >= nk || kl >= K) return;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      cs.q[ns] = *reinterpret_cast<const uint4*>(qrow[ns] + kl / 2);
+      cs.s[ns] = srow[ns][kl / 64];
+      cs.b[ns] = brow[ns][kl / 64];
+    }
+  };
+  auto load_a = [&](int s, uint4 (&ar)[AV]) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int idx = tid + 256 * i;
+      const int m = idx >> 4, c = idx & 15;
+      const int kk = s * kKS + c * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < rows && kk < K) {
+      if (s < nk && m < rows && kk < K) {
         if (GATE_UP) {
           const int tok = s_tok[m];
           if (tok >= 0) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tok) * K + kk);
@@ -109,42 +136,74 @@ __global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(GemmArgs a,
           v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + m) * K + kk);
         }
       }
-      *reinterpret_cast<uint4*>(&As[m * kLDA + c * 8]) = v;
+      ar[i] = v;
     }
-    __syncthreads();
-    if (!active) continue;
+  };
+  auto store_a = [&](int buf, const uint4 (&ar)[AV]) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int idx = tid + 256 * i;
+      const int m = idx >> 4, c = idx & 15;
+      if (m < tm) *reinterpret_cast<uint4*>(&As[buf][m * kLDA + c * 8]) = ar[i];
+    }
+  };
 
-    const int kl = kb + (lane >> 4) * 32;  // this lane's 32 reduction inputs
-    bf16x8 bfr[4][4];
+  f32x4 acc[M_MAX / 16][4];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      if (kl < K) {
-        const uint4 qv = *reinterpret_cast<const uint4*>(Q + static_cast<size_t>(wrow[ns]) * (K / 2) + kl / 2);
-        const size_t gi = static_cast<size_t>(wrow[ns]) * (K / 64) + kl / 64;
-        const float s = bf16_to_f32(Sc[gi]), b = bf16_to_f32(Bi[gi]);
-        bfr[ns][0] = as_bf16x8(dequant8(qv.x, s, b));
-        bfr[ns][1] = as_bf16x8(dequant8(qv.y, s, b));
-        bfr[ns][2] = as_bf16x8(dequant8(qv.z, s, b));
-        bfr[ns][3] = as_bf16x8(dequant8(qv.w, s, b));
-      } else {
+  for (int mt = 0; mt < M_MAX / 16; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[ns][j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one reduction step: rebuild this step's weights from the ring slot, refill
+  // the slot two steps ahead, run the MFMAs on the LDS buffer, move the next
+  // step's A tile into the other buffer
+  auto step = [&](int s, CodeSlot& cs, int buf, uint4 (&ar)[AV]) {
+    if (active) {
+      bf16x8 bfr[4][4];
+      const bool live = s * kKS + lk < K;
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        const float sc = bf16_to_f32(cs.s[ns]), bi = bf16_to_f32(cs.b[ns]);
+        bfr[ns][0] = as_bf16x8(live ? dequant8(cs.q[ns].x, sc, bi) : make_uint4(0, 0, 0, 0));
+        bfr[ns][1] = as_bf16x8(live ? dequant8(cs.q[ns].y, sc, bi) : make_uint4(0, 0, 0, 0));
+        bfr[ns][2] = as_bf16x8(live ? dequant8(cs.q[ns].z, sc, bi) : make_uint4(0, 0, 0, 0));
+        bfr[ns][3] = as_bf16x8(live ? dequant8(cs.q[ns].w, sc, bi) : make_uint4(0, 0, 0, 0));
+      }
+      load_codes(s + 2, cs);
+#pragma unroll
+      for (int mt = 0; mt < M_MAX / 16; ++mt) {
+        if (mt < mtiles) {
+          const uint16_t* ap = &As[buf][(mt * 16 + (lane & 15)) * kLDA + lk];
+          bf16x8 af[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[mt][ns] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfr[ns][j], acc[mt][ns], 0, 0, 0);
+        }
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < M_MAX / 16; ++mt) {
-      if (mt < mtiles) {
-        const uint16_t* ap = &As[(mt * 16 + (lane & 15)) * kLDA + (lane >> 4) * 32];
-        bf16x8 af[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfr[ns][j], acc[mt][ns], 0, 0, 0);
-      }
-    }
+    store_a(buf ^ 1, ar);
+    load_a(s + 2, ar);
+    __syncthreads();
+  };
+
+  // prologue: codes for steps 0 and 1 in flight, A(0) in LDS, A(1) in registers
+  CodeSlot c0, c1;
+  load_codes(0, c0);
+  load_codes(1, c1);
+  uint4 ar[AV];
+  load_a(0, ar);
+  store_a(0, ar);
+  load_a(1, ar);
+  __syncthreads();
+
+  for (int s = 0; s < nk; s += 2) {
+    step(s, c0, 0, ar);
+    if (s + 1 < nk) step(s + 1, c1, 1, ar);
   }
   if (!active) return;
 
@@ -172,8 +231,204 @@ __global__ __launch_bounds__(256) void w4_grouped_gemm_kernel(GemmArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-tile kernel: blocks of at most 32 rows (most experts of a prefill
+// chunk), where the work is bound by streaming and rebuilding weights rather
+// than by the matrix units.  Eight waves per workgroup; each wave owns two
+// 16-wide MFMA column slices (32 weight rows), so a wave needs few registers
+// and many waves per SIMD keep HBM loads in flight.  For gate/up, columns
+// 0..7 of a slice are gate rows and 8..15 the matching up rows, so SwiGLU pairs
+// lane n with lane n+8 in the epilogue.
+// ---------------------------------------------------------------------------
+struct SmallSlot {
+  uint4 q[2];
+  uint32_t sb[2];  // scale (low half) and bias (high half), bf16 bits
+};
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
+                                                            const uint16_t* __restrict__ src,
+                                                            uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
+  __shared__ int s_tok[kSmallM];
+
+  const int T = a.T, k = a.k;
+  const int Sk = T * k;
+  const int Rows = Sk + (a.n_shared ? T : 0);
+  const int K = GATE_UP ? a.H : a.I;
+  const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
+  const int bid = blockIdx.x / ntiles, nt = blockIdx.x % ntiles;
+  const int nblk = min(*a.n_blocks, a.max_blocks);
+  if (bid >= nblk) return;
+  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
+  const int G = blk.x, row0 = blk.y, rows = blk.z, tm = blk.w;
+  if (tm > kSmallM) return;  // a tall block: the big-tile kernel owns it
+  if (G < 0 || G >= a.E + (a.n_shared ? 1 : 0) || rows < 1 || rows > tm || (tm & 15) ||
+      row0 < 0 || row0 + rows > Rows) {
+    if (threadIdx.x == 0) status_set(a.status, MOE_STATUS_BAD_INDEX);
+    return;
+  }
+  const BankView& bk = (G < a.E) ? a.routed : a.shared;
+  const size_t ex = (G < a.E) ? static_cast<size_t>(G) : 0;
+  const int Nw = GATE_UP ? 2 * a.I : a.H;
+  const uint8_t* Q = (GATE_UP ? bk.gu_q : bk.dn_q) + ex * Nw * (K / 2);
+  const uint16_t* Sc = (GATE_UP ? bk.gu_s : bk.dn_s) + ex * Nw * (K / 64);
+  const uint16_t* Bi = (GATE_UP ? bk.gu_b : bk.dn_b) + ex * Nw * (K / 64);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15;
+  // output column of each slice (h column for gate/up, y column for down)
+  int ocol[2];
+  bool sl_on[2];
+  int wrow[2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    if (GATE_UP) {
+      const int c8 = nt * 128 + (wave * 2 + sl) * 8;
+      sl_on[sl] = c8 < a.I;
+      ocol[sl] = c8 + (n & 7);
+      wrow[sl] = sl_on[sl] ? ((n < 8) ? c8 + n : a.I + c8 + n - 8) : 0;
+    } else {
+      const int c16 = nt * 256 + (wave * 2 + sl) * 16;
+      sl_on[sl] = c16 < a.H;
+      ocol[sl] = c16 + n;
+      wrow[sl] = sl_on[sl] ? c16 + n : 0;
+    }
+  }
+  const bool active = sl_on[0];  // slice 1 is on only if slice 0 is
+
+  if (GATE_UP) {
+    if (tid < tm) {
+      int tok = -1;
+      if (tid < rows) {
+        const int r = row0 + tid;
+        tok = (r < Sk) ? a.sorted_slot[r] / k : r - Sk;
+        if (tok < 0 || tok >= T) {
+          status_set(a.status, MOE_STATUS_BAD_INDEX);
+          tok = -1;
+        }
+      }
+      s_tok[tid] = tok;
+    }
+    __syncthreads();
+  }
+
+  const int nk = (K + kKS - 1) / kKS;
+  const int mtiles = tm >> 4;
+  const int lk = (lane >> 4) * 32;
+
+  auto load_codes = [&](int s, SmallSlot& cs) {
+    const int kl = s * kKS + lk;
+    if (!active || s >= nk || kl >= K) return;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (!sl_on[sl]) continue;
+      cs.q[sl] = *reinterpret_cast<const uint4*>(Q + static_cast<size_t>(wrow[sl]) * (K / 2) + kl / 2);
+      const size_t gi = static_cast<size_t>(wrow[sl]) * (K / 64) + kl / 64;
+      cs.sb[sl] = static_cast<uint32_t>(Sc[gi]) | (static_cast<uint32_t>(Bi[gi]) << 16);
+    }
+  };
+  // A staging: tm rows x 16 chunks of 16 bytes, one chunk per thread
+  auto load_a = [&](int s) -> uint4 {
+    const int m = tid >> 4, c = tid & 15;
+    const int kk = s * kKS + c * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (s < nk && m < rows && kk < K) {
+      if (GATE_UP) {
+        const int tok = s_tok[m];
+        if (tok >= 0) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(tok) * K + kk);
+      } else {
+        v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + m) * K + kk);
+      }
+    }
+    return v;
+  };
+  auto store_a = [&](int buf, uint4 v) {
+    const int m = tid >> 4, c = tid & 15;
+    if (m < tm) *reinterpret_cast<uint4*>(&As[buf][m * kLDA + c * 8]) = v;
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int s, SmallSlot& cs, int buf, uint4& ar) {
+    if (active) {
+      bf16x8 bfr[2][4];
+      const bool live = s * kKS + lk < K;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const float sc = bf16_to_f32(cs.sb[sl] & 0xFFFFu), bi = bf16_to_f32(cs.sb[sl] >> 16);
+        const bool on = live && sl_on[sl];
+        bfr[sl][0] = as_bf16x8(on ? dequant8(cs.q[sl].x, sc, bi) : make_uint4(0, 0, 0, 0));
+        bfr[sl][1] = as_bf16x8(on ? dequant8(cs.q[sl].y, sc, bi) : make_uint4(0, 0, 0, 0));
+        bfr[sl][2] = as_bf16x8(on ? dequant8(cs.q[sl].z, sc, bi) : make_uint4(0, 0, 0, 0));
+        bfr[sl][3] = as_bf16x8(on ? dequant8(cs.q[sl].w, sc, bi) : make_uint4(0, 0, 0, 0));
+      }
+      load_codes(s + 2, cs);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        if (mt < mtiles) {
+          const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk];
+          bf16x8 af[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[mt][sl] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfr[sl][j], acc[mt][sl], 0, 0, 0);
+        }
+      }
+    }
+    store_a(buf ^ 1, ar);
+    ar = load_a(s + 2);
+    __syncthreads();
+  };
+
+  SmallSlot c0{}, c1{};
+  load_codes(0, c0);
+  load_codes(1, c1);
+  uint4 ar = load_a(0);
+  store_a(0, ar);
+  ar = load_a(1);
+  __syncthreads();
+  for (int s = 0; s < nk; s += 2) {
+    step(s, c0, 0, ar);
+    if (s + 1 < nk) step(s + 1, c1, 1, ar);
+  }
+  if (!active) return;
+
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    if (mt >= mtiles) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + (lane >> 4) * 4 + i;
+      const size_t r = static_cast<size_t>(row0 + m);
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const float v = acc[mt][sl][i];
+        if (GATE_UP) {
+          const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
+          if (n < 8 && m < rows && sl_on[sl]) {
+            const float hv = v / (1.0f + __expf(-v)) * u;   // SwiGLU: silu(g) * u
+            out[r * a.I + ocol[sl]] = f32_to_bf16(hv);
+          }
+        } else if (m < rows && sl_on[sl]) {
+          out[r * a.H + ocol[sl]] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+// Tall-tile kernel variant for a tile height bound (0: no tile exceeds kSmallM).
 int gemm_m_max_for(int tile_m_max) {
-  if (tile_m_max <= 64) return 64;
+  if (tile_m_max <= kSmallM) return 0;
   if (tile_m_max <= 128) return 128;
   return 256;
 }
@@ -182,16 +437,16 @@ template <bool GATE_UP>
 static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src, uint16_t* out,
                               hipStream_t stream) {
   const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
-  const dim3 grid(static_cast<unsigned>(a.max_blocks) * ntiles), block(256);
+  const dim3 grid(static_cast<unsigned>(a.max_blocks) * ntiles);
+  hipLaunchKernelGGL((w4_gemm_small_kernel<GATE_UP>), grid, dim3(512), 0, stream, a, src, out);
   switch (m_max) {
-    case 64:
-      hipLaunchKernelGGL((w4_grouped_gemm_kernel<64, GATE_UP>), grid, block, 0, stream, a, src, out);
-      break;
+    case 0:
+      break;  // every tile has at most kSmallM rows
     case 128:
-      hipLaunchKernelGGL((w4_grouped_gemm_kernel<128, GATE_UP>), grid, block, 0, stream, a, src, out);
+      hipLaunchKernelGGL((w4_grouped_gemm_kernel<128, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
       break;
     default:
-      hipLaunchKernelGGL((w4_grouped_gemm_kernel<256, GATE_UP>), grid, block, 0, stream, a, src, out);
+      hipLaunchKernelGGL((w4_grouped_gemm_kernel<256, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
       break;
   }
   return hipGetLastError();
