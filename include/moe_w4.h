@@ -63,7 +63,7 @@ extern "C" {
  *   E          routed experts, 1..1024
  *   k          experts selected per token, 1..min(E, 32)
  *   n_shared   always-on shared experts, 0 or 1 (same shape as a routed expert)
- *   tile_m_max largest GEMM tile height, a multiple of tile_gran in 16..256
+ *   tile_m_max largest GEMM tile height, a multiple of tile_gran in 16..128
  *   tile_gran  tile height granularity, 16 or 32
  * A slot is (token t, rank j < k) with id t*k + j.  The grouped GEMMs work on
  * Rows = T*k + n_shared*T rows: the routed slots in expert order, then one
@@ -75,23 +75,31 @@ typedef struct moe_dims {
 } moe_dims;
 
 /*
- * One bank of n experts in the packed groupwise-affine 4-bit layout [LB, "Model
- * structure ..."].  Each matrix is [n][rows][K] with rows = output features and
- * K = input features; every row is cut into groups of 64 consecutive inputs
- * that share one bfloat16 scale and one bfloat16 bias.  Byte b of a row holds
- * input 2b in its low nibble and 2b+1 in its high nibble; codes q are unsigned
- * 0..15 and the weight is w = bf16(fma(q, scale, bias)) (float32 fused
- * multiply-add, rounded once to nearest-even bfloat16).
- *   gu_q [n][2I][H/2] uint8   gate rows 0..I-1, up rows I..2I-1   (16-byte aligned)
- *   gu_s, gu_b [n][2I][H/64] bfloat16                               (4-byte aligned)
- *   dn_q [n][H][I/2] uint8                                          (16-byte aligned)
- *   dn_s, dn_b [n][H][I/64] bfloat16                                (4-byte aligned)
+ * Weights.  The checkpoint format [LB, "Model structure ..."] of one matrix of
+ * N output rows and K inputs is groupwise-affine 4-bit ("canonical layout"):
+ *   q [N][K/2] uint8: byte b of a row holds input 2b in its low nibble and
+ *                     2b+1 in its high nibble; codes are unsigned 0..15
+ *   s, b [N][K/64] bfloat16: scale and bias of each group of 64 consecutive
+ *                     inputs of a row
+ * and a weight is w = bf16(fma(q, s, b)) (float32 fused multiply-add, rounded
+ * once to nearest-even bfloat16).  Gate/up matrices have N = 2I rows (gate
+ * rows 0..I-1, up rows I..2I-1) and K = H; down matrices N = H, K = I.
+ *
+ * The GEMMs read the same bytes permuted into a streaming layout, written
+ * once by moe_w4_pack: for every 16-row slice and every 128-input step, one
+ * 1152-byte block holding the slice's codes in the order the GPU lanes load
+ * them followed by the (scale, bias) pairs, with inputs past K padded as code
+ * 0, scale 0, bias 0; gate/up slices pair 8 gate rows with their 8 up rows.
+ * The packed matrix has moe_w4_packed_bytes(N, K) bytes (4.5 bits per weight
+ * when K is a multiple of 128).
+ *
+ * One bank of n experts, packed (both pointers 16-byte aligned):
+ *   gu  n consecutive packed gate/up matrices, moe_w4_packed_bytes(2I, H) each
+ *   dn  n consecutive packed down matrices, moe_w4_packed_bytes(H, I) each
  */
 typedef struct moe_w4_bank {
-  const uint8_t *gu_q;
-  const uint16_t *gu_s, *gu_b;
-  const uint8_t *dn_q;
-  const uint16_t *dn_s, *dn_b;
+  const uint8_t *gu;
+  const uint8_t *dn;
 } moe_w4_bank;
 
 /*
@@ -128,6 +136,21 @@ typedef struct moe_route_out {
   void *ws;
   size_t ws_bytes;
 } moe_route_out;
+
+/* Bytes of one packed matrix of `rows` output rows (a multiple of 16) and K
+ * inputs (a multiple of 64); 0 if the sizes are invalid. */
+size_t moe_w4_packed_bytes(int32_t rows, int32_t K);
+
+/*
+ * moe_w4_pack - one-time repack of n canonical-layout matrices (consecutive in
+ * q, s, b) into the streaming layout, n * moe_w4_packed_bytes(rows, K) bytes at
+ * `packed`.  gate_up = 1 pairs gate row i with up row rows/2 + i (use it for
+ * gate/up matrices), 0 keeps rows in order (down matrices).
+ *   q (16-byte aligned), s, b (2-byte aligned), packed (16-byte aligned): device.
+ *   rows a positive multiple of 16, K a positive multiple of 64, n >= 0.
+ */
+int moe_w4_pack(int32_t n, int32_t rows, int32_t K, int32_t gate_up, const uint8_t *q,
+                const uint16_t *s, const uint16_t *b, uint8_t *packed, void *stream);
 
 /* MOE_W4_ABI_VERSION of the loaded library. */
 int moe_abi_version(void);
@@ -167,7 +190,8 @@ int moe_route(const moe_dims *d, const uint16_t *x, const float *w_router, const
  * row - T*k for shared rows).
  *   x        [T][H] bfloat16, the same activations given to moe_route
  *   r        tables from moe_route (blocks, n_blocks, sorted_slot, status)
- *   routed   bank of E experts;  shared  bank of 1 expert or NULL if n_shared = 0
+ *   routed   packed bank of E experts;  shared  packed bank of 1 expert, or NULL
+ *            if n_shared = 0
  *   h        [Rows][I] bfloat16 output (16-byte aligned)
  */
 int moe_w4_gate_up(const moe_dims *d, const uint16_t *x, const moe_route_out *r,
@@ -199,7 +223,7 @@ int moe_combine(const moe_dims *d, const moe_route_out *r, const uint16_t *y_slo
                 void *stream);
 
 /*
- * moe_w4_dequant - expand a packed [rows][K] matrix to bfloat16 in memory, with
+ * moe_w4_dequant - expand a canonical-layout [rows][K] matrix to bfloat16 in memory, with
  * the same device reconstruction the GEMMs use.  Diagnostic: it materialises
  * exactly the array the fused GEMMs avoid, for bit-exactness checks and for the
  * unfused comparison [LB, "Prefill: ..."].

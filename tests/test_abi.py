@@ -52,7 +52,7 @@ def test_max_blocks_and_workspace():
 
 @pytest.mark.parametrize("field,value", [("H", 96), ("I", 0), ("E", 0), ("E", 2000), ("k", 0),
                                          ("k", 33), ("n_shared", 2), ("tile_m_max", 24),
-                                         ("tile_m_max", 512), ("tile_gran", 8), ("T", -1)])
+                                         ("tile_m_max", 256), ("tile_gran", 8), ("T", -1)])
 def test_invalid_dims_rejected(field, value):
     d = full(4)
     setattr(d, field, value)
@@ -90,10 +90,10 @@ def test_ffn_and_combine_validation_codes():
     L = moe.lib()
     d = full(4)
     out = _route_out()
-    bank = Bank(0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000)
+    bank = Bank(0x2000, 0x3000)
     assert L.moe_w4_gate_up(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
                             None, 0x8000, None) == -1          # shared bank missing
-    mis = Bank(0x2008, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000)
+    mis = Bank(0x2008, 0x3000)
     assert L.moe_w4_gate_up(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(mis),
                             ctypes.byref(bank), 0x8000, None) == -2
     assert L.moe_w4_down(ctypes.byref(d), ctypes.byref(out), ctypes.byref(bank),
@@ -106,3 +106,18 @@ def test_ffn_and_combine_validation_codes():
                                 ctypes.byref(bank), 0x8000, 0x9000, None) == 0
     assert L.moe_w4_dequant(4, 100, 0x1000, 0x2000, 0x3000, 0x4000, None) == -1
     assert L.moe_w4_dequant(0, 64, 0x1000, 0x2000, 0x3000, 0x4000, None) == 0
+
+
+def test_pack_sizes_and_validation():
+    L = moe.lib()
+    # one 1152-byte block per (16-row slice, 128-input step)
+    assert moe.moe_w4_packed_bytes(1024, 2048) == 64 * 16 * 1152
+    assert moe.moe_w4_packed_bytes(1024, 2048) * 8 == 1024 * 2048 * 4.5
+    assert moe.moe_w4_packed_bytes(2048, 512) == 128 * 4 * 1152
+    assert moe.moe_w4_packed_bytes(16, 64) == 1152          # K tail padded to a full step
+    assert moe.moe_w4_packed_bytes(24, 64) == 0             # rows not a multiple of 16
+    assert moe.moe_w4_packed_bytes(16, 96) == 0             # K not a multiple of 64
+    assert L.moe_w4_pack(1, 16, 64, 2, 0x1000, 0x2000, 0x3000, 0x4000, None) == -1
+    assert L.moe_w4_pack(1, 16, 64, 0, 0x1008, 0x2000, 0x3000, 0x4000, None) == -2
+    assert L.moe_w4_pack(1, 16, 64, 0, 0x1000, 0x2000, 0x3000, 0x4008, None) == -2
+    assert L.moe_w4_pack(0, 16, 64, 0, 0x1000, 0x2000, 0x3000, 0x4000, None) == 0

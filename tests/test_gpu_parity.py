@@ -131,19 +131,67 @@ def check_layer(cfg, T=None, t0=0, tile_m_max=128, sample=None, banks=None, labe
 # ----------------------------------------------------------------------------- dequant
 
 def test_dequant_bit_exact(full_banks):
-    routed_np, _, routed_dev, _ = full_banks
+    routed_np = full_banks[0]
     note("case dequant expert 3 gate/up and down")
     for part, rows, K in (("gu", 1024, 2048), ("dn", 2048, 512)):
-        q = routed_dev.t[f"{part}_q"][3]
-        s = routed_dev.t[f"{part}_s"][3]
-        b = routed_dev.t[f"{part}_b"][3]
+        q, s_, b = (dev(routed_np[f"{part}_{n}"][3]) for n in ("q", "s", "b"))
         out = torch.empty((rows, K), dtype=torch.int16, device="cuda")
-        moe.moe_w4_dequant(rows, K, q, s, b, out)
+        moe.moe_w4_dequant(rows, K, q, s_, b, out)
         torch.cuda.synchronize()
         got = bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
         ref = oracle.dequant(routed_np[f"{part}_q"][3], routed_np[f"{part}_s"][3],
                              routed_np[f"{part}_b"][3])
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def unpack_host(packed, N, K, gate_up):
+    """Decode the streaming layout (as documented in include/moe_w4.h) back to
+    canonical q, s, b arrays, independently of the device code."""
+    nk = -(-K // 128)
+    blocks = packed.reshape(N // 16, nk, 1152)
+    q = np.zeros((N, K // 2), dtype=np.uint8)
+    s = np.zeros((N, K // 64), dtype=np.uint16)
+    b = np.zeros((N, K // 64), dtype=np.uint16)
+    for c in range(N // 16):
+        rows = [(c * 8 + r if r < 8 else N // 2 + c * 8 + r - 8) if gate_up else c * 16 + r
+                for r in range(16)]
+        for st in range(nk):
+            blk = blocks[c, st]
+            codes = blk[:1024].reshape(64, 16)
+            sb = blk[1024:].view(np.uint32).reshape(2, 16)
+            for lane in range(64):
+                r, g = lane % 16, lane // 16
+                k0 = st * 128 + g * 32
+                if k0 < K:
+                    q[rows[r], k0 // 2:k0 // 2 + 16] = codes[lane]
+                else:
+                    assert not codes[lane].any()
+            for gg in range(2):
+                grp = st * 2 + gg
+                for r in range(16):
+                    if grp * 64 < K:
+                        s[rows[r], grp] = sb[gg, r] & 0xFFFF
+                        b[rows[r], grp] = sb[gg, r] >> 16
+                    else:
+                        assert sb[gg, r] == 0
+    return q, s, b
+
+
+@pytest.mark.parametrize("N,K,gate_up", [(64, 256, True), (32, 192, False), (48, 64, False)])
+def test_pack_layout(N, K, gate_up):
+    note(f"case pack layout N={N} K={K} gate_up={gate_up}")
+    rng = np.random.default_rng(N + K)
+    q = rng.integers(0, 256, (2, N, K // 2), dtype=np.uint8)
+    s_ = rng.integers(0, 65536, (2, N, K // 64), dtype=np.uint16)
+    b = rng.integers(0, 65536, (2, N, K // 64), dtype=np.uint16)
+    nbytes = moe.moe_w4_packed_bytes(N, K)
+    out = torch.zeros((2, nbytes), dtype=torch.uint8, device="cuda")
+    moe.moe_w4_pack(2, N, K, gate_up, dev(q), dev(s_), dev(b), out)
+    torch.cuda.synchronize()
+    packed = out.cpu().numpy()
+    for e in range(2):
+        uq, us, ub = unpack_host(packed[e], N, K, gate_up)
+        assert np.array_equal(uq, q[e]) and np.array_equal(us, s_[e]) and np.array_equal(ub, b[e])
 
 
 def test_dequant_general_bias():
@@ -196,7 +244,7 @@ def test_prefill2048_zipf(full_banks):
     assert (counts == 0).sum() >= 1 and (counts > 200).sum() >= 1
 
 
-@pytest.mark.parametrize("tile_m_max", [32, 256])
+@pytest.mark.parametrize("tile_m_max", [32, 64])
 def test_prefill2048_zipf_tiles(full_banks, tile_m_max):
     check_layer("prefill2048_zipf", tile_m_max=tile_m_max, banks=full_banks, sample=12,
                 label=f"zipf M={tile_m_max}")

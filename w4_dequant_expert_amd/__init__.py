@@ -26,6 +26,8 @@ from .moe import (  # noqa: F401
     moe_route,
     moe_route_ws_bytes,
     moe_w4_dequant,
+    moe_w4_pack,
+    moe_w4_packed_bytes,
     moe_w4_down,
     moe_w4_gate_up,
     strerror,

@@ -39,7 +39,7 @@ int validate_dims(const moe_dims* d) {
   if (d->k < 1 || d->k > kMaxK || d->k > d->E) return MOE_EINVAL;
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_EINVAL;
   if (d->tile_gran != 16 && d->tile_gran != 32) return MOE_EINVAL;
-  if (d->tile_m_max < 16 || d->tile_m_max > 256 || d->tile_m_max % d->tile_gran) return MOE_EINVAL;
+  if (d->tile_m_max < 16 || d->tile_m_max > 128 || d->tile_m_max % d->tile_gran) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -82,17 +82,19 @@ int validate_route_out(const moe_route_out* r, bool for_route) {
 }
 
 int validate_bank(const moe_w4_bank* b) {
-  if (!b || !b->gu_q || !b->gu_s || !b->gu_b || !b->dn_q || !b->dn_s || !b->dn_b) return MOE_EINVAL;
-  if (!aligned(b->gu_q, 16) || !aligned(b->dn_q, 16) || !aligned(b->gu_s, 4) ||
-      !aligned(b->gu_b, 4) || !aligned(b->dn_s, 4) || !aligned(b->dn_b, 4))
-    return MOE_EALIGN;
+  if (!b || !b->gu || !b->dn) return MOE_EINVAL;
+  if (!aligned(b->gu, 16) || !aligned(b->dn, 16)) return MOE_EALIGN;
   return MOE_OK;
 }
 
 BankView view(const moe_w4_bank* b) {
   BankView v{};
-  if (b) v = BankView{b->gu_q, b->gu_s, b->gu_b, b->dn_q, b->dn_s, b->dn_b};
+  if (b) v = BankView{b->gu, b->dn};
   return v;
+}
+
+bool pack_dims_ok(int32_t rows, int32_t K) {
+  return rows > 0 && rows % 16 == 0 && rows <= (1 << 20) && K > 0 && K % 64 == 0 && K <= (1 << 16);
 }
 
 int32_t max_blocks_of(const moe_dims& d) {
@@ -251,6 +253,22 @@ int moe_combine(const moe_dims* d, const moe_route_out* r, const uint16_t* y_slo
   (void)hipGetLastError();
   return launched(launch_combine(d->T, d->H, d->k, d->n_shared, r->topk_w, r->slot_pos, y_slots, y,
                                  r->status, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_w4_packed_bytes(int32_t rows, int32_t K) {
+  return pack_dims_ok(rows, K) ? pack_bytes(rows, K) : 0;
+}
+
+int moe_w4_pack(int32_t n, int32_t rows, int32_t K, int32_t gate_up, const uint8_t* q,
+                const uint16_t* s, const uint16_t* b, uint8_t* packed, void* stream) {
+  if (n < 0 || !pack_dims_ok(rows, K) || (gate_up != 0 && gate_up != 1)) return MOE_EINVAL;
+  if (!q || !s || !b || !packed) return MOE_EINVAL;
+  if (!aligned(q, 16) || !aligned(s, 2) || !aligned(b, 2) || !aligned(packed, 16)) return MOE_EALIGN;
+  if (n == 0) return MOE_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return launched(launch_pack(n, rows, K, gate_up, q, s, b, packed, static_cast<hipStream_t>(stream)));
 }
 
 int moe_w4_dequant(int32_t rows, int32_t K, const uint8_t* q, const uint16_t* s, const uint16_t* b,

@@ -40,16 +40,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
 //     exactly;
 //   - one float32 fused multiply-add per weight, then one round to bfloat16.
 __device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b) {
-  const uint32_t ev = w & 0x0F0F0F0Fu;          // codes 0,2,4,6
-  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // codes 1,3,5,7
-  float f0 = __builtin_fmaf(static_cast<float>(ev & 0xFFu), s, b);
-  float f1 = __builtin_fmaf(static_cast<float>(od & 0xFFu), s, b);
-  float f2 = __builtin_fmaf(static_cast<float>((ev >> 8) & 0xFFu), s, b);
-  float f3 = __builtin_fmaf(static_cast<float>((od >> 8) & 0xFFu), s, b);
-  float f4 = __builtin_fmaf(static_cast<float>((ev >> 16) & 0xFFu), s, b);
-  float f5 = __builtin_fmaf(static_cast<float>((od >> 16) & 0xFFu), s, b);
-  float f6 = __builtin_fmaf(static_cast<float>(ev >> 24), s, b);
-  float f7 = __builtin_fmaf(static_cast<float>(od >> 24), s, b);
+  uint32_t ev = w & 0x0F0F0F0Fu;          // codes 0,2,4,6, one per byte
+  uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // codes 1,3,5,7
+  // Opaque to the optimiser, so that each byte below widens with one
+  // v_cvt_f32_ubyteN instead of a field extract plus a conversion.
+  asm("" : "+v"(ev));
+  asm("" : "+v"(od));
+  const float f0 = __builtin_fmaf(static_cast<float>(ev & 0xFFu), s, b);
+  const float f1 = __builtin_fmaf(static_cast<float>(od & 0xFFu), s, b);
+  const float f2 = __builtin_fmaf(static_cast<float>((ev >> 8) & 0xFFu), s, b);
+  const float f3 = __builtin_fmaf(static_cast<float>((od >> 8) & 0xFFu), s, b);
+  const float f4 = __builtin_fmaf(static_cast<float>((ev >> 16) & 0xFFu), s, b);
+  const float f5 = __builtin_fmaf(static_cast<float>((od >> 16) & 0xFFu), s, b);
+  const float f6 = __builtin_fmaf(static_cast<float>(ev >> 24), s, b);
+  const float f7 = __builtin_fmaf(static_cast<float>(od >> 24), s, b);
   uint4 r;
   r.x = pack_bf16x2(f0, f1);
   r.y = pack_bf16x2(f2, f3);
@@ -58,20 +62,47 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b) {
   return r;
 }
 
+// Wave-uniform copy of a value the compiler cannot prove uniform.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ void status_set(uint32_t* status, uint32_t bits) {
   if (status) atomicOr(status, bits);
 }
 
-// Pointers of one expert bank (device) as seen by the kernels.
+// ---------------------------------------------------------------------------
+// Packed weight layout (written once by moe_w4_pack, read by the GEMMs).
+//
+// A matrix of N output rows and K inputs is cut into N/16 slices of 16 rows
+// and ceil(K/128) steps of 128 inputs.  Each (slice, step) is one contiguous
+// block of kPackBlock bytes, blocks ordered slice-major:
+//   bytes [0, 1024): lane l (0..63) of a wave finds at l*16 the 16 code bytes
+//     (32 consecutive inputs step*128 + (l/16)*32 ..) of row (l mod 16) of the
+//     slice, in the canonical nibble order;
+//   bytes [1024, 1152): 32 dwords; dword g*16 + r holds the scale (low half)
+//     and bias (high half) of row r for inputs step*128 + g*64 .. +63.
+// Inputs past K are code 0 with scale 0 and bias 0 (they rebuild to +0).
+// Gate/up matrices interleave gate and up rows: slice c holds gate rows
+// 8c..8c+7 as rows 0..7 and the matching up rows I+8c.. as rows 8..15, so a
+// lane's gate and up outputs sit 8 lanes apart.  Down matrices are straight:
+// slice c holds rows 16c..16c+15.
+// Every wave load is a whole 1024-byte (or 128-byte) run and every byte is
+// read once per use, which is what lets the GEMMs stream at HBM speed.
+// ---------------------------------------------------------------------------
+constexpr int kKS = 128;             // inputs per step
+constexpr int kPackBlock = 1152;     // bytes per (slice, step) block
+constexpr int kPackScales = 1024;    // offset of the scale/bias dwords
+
+__host__ __device__ inline int pack_steps(int K) { return (K + kKS - 1) / kKS; }
+__host__ __device__ inline size_t pack_bytes(int N, int K) {
+  return static_cast<size_t>(N / 16) * pack_steps(K) * kPackBlock;
+}
+
+// Packed matrices of one expert bank (device) as seen by the kernels.
 struct BankView {
-  const uint8_t* gu_q;
-  const uint16_t* gu_s;
-  const uint16_t* gu_b;
-  const uint8_t* dn_q;
-  const uint16_t* dn_s;
-  const uint16_t* dn_b;
+  const uint8_t* gu;  // [n][pack_bytes(2I, H)]
+  const uint8_t* dn;  // [n][pack_bytes(H, I)]
 };
 
 }  // namespace moe

@@ -20,7 +20,8 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWS, MOE_EDEVICE, MOE_ELAUNCH = 0, -1, -2, -
 STATUS_NAN_LOGIT, STATUS_BAD_INDEX, STATUS_BLOCK_OVERFLOW = 1, 2, 4
 
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_bytes", "moe_route",
-            "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_combine", "moe_w4_dequant")
+            "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_combine", "moe_w4_dequant",
+            "moe_w4_packed_bytes", "moe_w4_pack")
 
 
 class Dims(ctypes.Structure):
@@ -29,7 +30,8 @@ class Dims(ctypes.Structure):
 
 
 class Bank(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b")]
+    """Packed bank: gate/up and down matrices of n experts."""
+    _fields_ = [("gu", ctypes.c_void_p), ("dn", ctypes.c_void_p)]
 
 
 class RouteOut(ctypes.Structure):
@@ -81,6 +83,11 @@ def lib():
         L.moe_combine.argtypes = [P(Dims), P(RouteOut), vp, vp, vp]
         L.moe_w4_dequant.restype = ctypes.c_int
         L.moe_w4_dequant.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
+        L.moe_w4_packed_bytes.restype = ctypes.c_size_t
+        L.moe_w4_packed_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.moe_w4_pack.restype = ctypes.c_int
+        L.moe_w4_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -160,6 +167,15 @@ def moe_w4_dequant(rows: int, K: int, q, s, b, out, stream=None):
            "moe_w4_dequant")
 
 
+def moe_w4_packed_bytes(rows: int, K: int) -> int:
+    return lib().moe_w4_packed_bytes(rows, K)
+
+
+def moe_w4_pack(n: int, rows: int, K: int, gate_up: bool, q, s, b, packed, stream=None):
+    _check(lib().moe_w4_pack(n, rows, K, 1 if gate_up else 0, _ptr(q), _ptr(s), _ptr(b),
+                             _ptr(packed), _stream(stream)), "moe_w4_pack")
+
+
 # --------------------------------------------------------------------- device buffers
 
 def make_dims(T, H, I, E, k, n_shared, tile_m_max=128, tile_gran=16) -> Dims:
@@ -175,25 +191,41 @@ def _dev(a: np.ndarray, device):
 
 
 class DeviceBank:
-    """An expert bank uploaded to device memory (bit patterns, packed layout)."""
+    """An expert bank resident in device memory in the packed streaming layout.
 
-    NAMES = ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b")
+    The canonical-layout arrays (numpy, as in a checkpoint) are uploaded once,
+    repacked on the device by moe_w4_pack, and released.
+    """
+
+    CANON = ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b")
 
     def __init__(self, bank: dict, device="cuda"):
-        self.t = {n: _dev(bank[n], device) for n in self.NAMES}
-        self.n = bank["gu_q"].shape[0]
-        self.c = Bank(*[self.t[n].data_ptr() for n in self.NAMES])
+        import torch
+        n, two_i, half_h = bank["gu_q"].shape
+        H = 2 * half_h
+        I = two_i // 2
+        self.n, self.H, self.I = n, H, I
+        canon = {k: _dev(bank[k], device) for k in self.CANON}
+        gu = torch.empty((n, moe_w4_packed_bytes(2 * I, H)), dtype=torch.uint8, device=device)
+        dn = torch.empty((n, moe_w4_packed_bytes(H, I)), dtype=torch.uint8, device=device)
+        moe_w4_pack(n, 2 * I, H, True, canon["gu_q"], canon["gu_s"], canon["gu_b"], gu)
+        moe_w4_pack(n, H, I, False, canon["dn_q"], canon["dn_s"], canon["dn_b"], dn)
+        torch.cuda.current_stream().synchronize()
+        del canon
+        self.t = {"gu": gu, "dn": dn}
+        self.c = Bank(gu.data_ptr(), dn.data_ptr())
 
     @classmethod
-    def from_tensors(cls, tensors: dict):
+    def from_tensors(cls, tensors: dict, n, H, I):
         self = cls.__new__(cls)
         self.t = tensors
-        self.n = tensors["gu_q"].shape[0]
-        self.c = Bank(*[tensors[n].data_ptr() for n in cls.NAMES])
+        self.n, self.H, self.I = n, H, I
+        self.c = Bank(tensors["gu"].data_ptr(), tensors["dn"].data_ptr())
         return self
 
     def clone(self):
-        return DeviceBank.from_tensors({n: v.clone() for n, v in self.t.items()})
+        return DeviceBank.from_tensors({k: v.clone() for k, v in self.t.items()}, self.n, self.H,
+                                       self.I)
 
     def nbytes(self) -> int:
         return sum(v.numel() * v.element_size() for v in self.t.values())
