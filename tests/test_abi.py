@@ -45,7 +45,7 @@ def test_max_blocks_and_workspace():
         d = full(T)
         assert moe.moe_max_blocks(d) == oracle.max_blocks(T, 256, 8, 1, 128)
     d = full(2048)
-    assert moe.moe_route_ws_bytes(d) >= 2048 * 256 * 4 + 2048 * 8 * 4
+    assert moe.moe_route_ws_bytes(d) >= 2048 * 256 * 4 + 2 * 64 * 256 * 4
     assert moe.moe_max_blocks(moe.make_dims(4, 64, 64, 8, 9, 0)) == -1      # k > E
     assert moe.moe_route_ws_bytes(moe.make_dims(4, 100, 64, 8, 2, 0)) == 0  # H % 64
 

@@ -46,20 +46,20 @@ int validate_dims(const moe_dims* d) {
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-  size_t logits, partial, local_rank, total;
+  size_t logits, bits, pref, total;
 };
 
 WsLayout ws_layout(const moe_dims& d, bool need_logits) {
-  const size_t T = d.T, E = d.E, k = d.k;
-  const size_t nwg = (T + route_tokens_per_wg(d.k) - 1) / route_tokens_per_wg(d.k);
+  const size_t T = d.T, E = d.E;
+  const size_t W = (T + 31) / 32;
   WsLayout L;
   size_t off = 0;
   L.logits = off;
   off += need_logits ? align256(T * E * 4) : 0;
-  L.partial = off;
-  off += align256(nwg * E * 4);
-  L.local_rank = off;
-  off += align256(T * k * 4);
+  L.bits = off;
+  off += align256(W * E * 4);
+  L.pref = off;
+  off += align256(W * E * 4);
   L.total = off;
   return L;
 }
@@ -186,8 +186,8 @@ int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const
   rb.slot_pos = out->slot_pos;
   rb.blocks = out->blocks;
   rb.n_blocks = out->n_blocks;
-  rb.partial = reinterpret_cast<int32_t*>(ws + L.partial);
-  rb.local_rank = reinterpret_cast<int32_t*>(ws + L.local_rank);
+  rb.bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+  rb.pref = reinterpret_cast<int32_t*>(ws + L.pref);
   rb.status = out->status;
   rb.max_blocks = max_blocks_of(*d);
   (void)hipGetLastError();

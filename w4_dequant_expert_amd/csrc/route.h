@@ -8,9 +8,6 @@ namespace moe {
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 
-// Tokens per top-k workgroup: its slots (tokens * k) fit one 256-lane workgroup.
-inline int route_tokens_per_wg(int k) { return 256 / k; }
-
 struct RouteBuffers {
   float* logits;         // [T][E]
   int32_t* topk_idx;     // [T][k]
@@ -21,8 +18,8 @@ struct RouteBuffers {
   int32_t* slot_pos;     // [T*k]
   int32_t* blocks;       // [max_blocks][4]
   int32_t* n_blocks;     // [1]
-  int32_t* partial;      // [n_route_wg][E]   (workspace)
-  int32_t* local_rank;   // [T*k]             (workspace)
+  uint32_t* bits;        // [ceil(T/32)][E] token bitmask per expert   (workspace)
+  int32_t* pref;         // [ceil(T/32)][E] tokens before each word     (workspace)
   uint32_t* status;
   int max_blocks;
 };

@@ -1,75 +1,99 @@
 // GPU-resident routing for the MoE expert layer on gfx950: router scores,
-// top-k with renormalised softmax weights, per-workgroup histograms with
-// wavefront ballot ranks, one exclusive scan, the stable scatter and the tile
-// block map.  Everything stays on the device: the grouped GEMMs read the block
-// map and its length from memory, so nothing returns to the host between the
-// router and the GEMMs ["Lily Beats MLX-LM 1.35x on Decode", "Prefill: fusing
-// dequantisation and keeping routing GPU-resident"].
+// top-k with renormalised softmax weights, the expert histogram, one exclusive
+// scan, the stable scatter and the tile block map.  Everything stays on the
+// device: the grouped GEMMs read the block map and its length from memory, so
+// nothing returns to the host between the router and the GEMMs ["Lily Beats
+// MLX-LM 1.35x on Decode", "Prefill: fusing dequantisation and keeping routing
+// GPU-resident"; "Introduction: Revolutionizing Local AI Inference on Apple
+// Silicon", "Optimizing Prefill Operations"].
+//
+// Three kernels on one stream:
+//   K1 router scores (float32, fixed evaluation order) and clearing of the
+//      token bitmask;
+//   K2 top-k and weights, 16 lanes per token with DPP row reductions; every
+//      selection sets its token's bit in a [token word][expert] bitmask with
+//      an atomic OR (order-independent, hence deterministic);
+//   K3 one workgroup: per-expert popcount prefixes over the bitmask give the
+//      histogram and every slot's stable rank, then the exclusive scan, the
+//      block map and the scatter.
+// A token selects an expert at most once, so ordering an expert's slots by
+// token is the same as ordering them by slot id: the rank of slot (t, j) in
+// its expert e is the number of tokens before t that selected e.
 #include "route.h"
 
-#include <float.h>
 #include <math.h>
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// K1: router scores.  Workgroup tile: kRT tokens x kRE experts, 16 waves of
-// 8 tokens x 8 experts.  Within a wave, lane m owns partial m of every one of
-// its 64 outputs: a float32 fma chain over inputs h = m, m+64, m+128, ...  The
-// 64 partials of each output are then combined by a transposed butterfly over
-// the lanes whose pairing is exactly the tree p[i] += p[i+s], s = 32..1, so
-// every score has one fixed, host-reproducible evaluation order.  x and the
-// router weights are staged through LDS in chunks of kCH x 64 inputs.
+// K1: router scores.  A wave computes a tile of TW tokens x EW experts; lane m
+// owns partial m of every one of its outputs: a float32 fma chain over inputs
+// h = m, m+64, m+128, ...  The 64 partials of each output are combined by a
+// transposed butterfly across the lanes whose pairing is exactly the tree
+// p[i] += p[i+s], s = 32..1, so every score has one fixed evaluation order
+// that a host implementation reproduces bit for bit.  x (as float32,
+// transposed) and the router weights are staged through LDS, CH chunks of 64
+// inputs at a time.
 // ---------------------------------------------------------------------------
-constexpr int kTW = 8, kEW = 8;         // per-lane tile
-constexpr int kWT = 4, kWE = 4;         // waves per workgroup (tokens x experts)
-constexpr int kRT = kTW * kWT;          // 32 tokens per workgroup
-constexpr int kRE = kEW * kWE;          // 32 experts per workgroup
-constexpr int kCH = 2;                  // 64-input chunks per LDS stage
-constexpr int kPadT = kRT + 4, kPadE = kRE + 4;
+constexpr int kTW = 8, kEW = 8;  // per-lane tile: 64 outputs
 
-__global__ __launch_bounds__(1024) void router_scores_kernel(int T, int H, int E, int vec_wr,
-                                                             const uint16_t* __restrict__ x,
-                                                             const float* __restrict__ wr,
-                                                             const float* __restrict__ bias,
-                                                             float* __restrict__ logits,
-                                                             uint32_t* __restrict__ status) {
-  __shared__ float xs[kCH][64][kPadT];  // x chunk, transposed: [input][token]
-  __shared__ float ws[kCH][64][kPadE];  // router chunk: [input][expert]
+template <int WT, int WE, int CH>
+__global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
+    int T, int H, int E, int vec_wr, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, uint32_t* __restrict__ bits,
+    int nbits, uint32_t* __restrict__ status) {
+  constexpr int NT = WT * WE * 64;
+  constexpr int RT = kTW * WT, RE = kEW * WE;  // workgroup tile
+  constexpr int PT = RT + 4, PE = RE + 4;      // padded LDS rows
+  __shared__ float xs[CH][64][PT];  // x chunk, transposed: [input][token]
+  __shared__ float ws[CH][64][PE];  // router chunk: [input][expert]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wt = wave % kWT, we = wave / kWT;
-  const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRE;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && status) *status = 0u;
+  const int wt = wave % WT, we = wave / WT;
+  const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
+
+  {  // clear the token bitmask of K2 and the status word (stream-ordered before K2)
+    const long long gid = (static_cast<long long>(blockIdx.y) * gridDim.x + blockIdx.x) * NT + tid;
+    const long long gsz = static_cast<long long>(gridDim.x) * gridDim.y * NT;
+    for (long long i = gid; i < nbits; i += gsz) bits[i] = 0u;
+    if (gid == 0 && status) *status = 0u;
+  }
 
   float acc[kTW * kEW];
 #pragma unroll
   for (int o = 0; o < kTW * kEW; ++o) acc[o] = 0.0f;
 
+  // Staging with fixed per-thread counts, so every load of a chunk is issued
+  // before any of them is waited for; the next chunk is loaded into registers
+  // while the current one is multiplied.
+  constexpr int XN = RT * CH * 8;          // 16-byte x loads per chunk
+  constexpr int WN = CH * 64 * (RE / 4);   // 16-byte router loads per chunk
+  constexpr int XI = (XN + NT - 1) / NT, WI = (WN + NT - 1) / NT;
   const int nchunk = H / 64;
-  for (int c0 = 0; c0 < nchunk; c0 += kCH) {
-    __syncthreads();
-    for (int idx = tid; idx < kRT * kCH * 8; idx += 1024) {  // stage x, 8 bf16 per load
-      const int t = idx / (kCH * 8), part = idx % (kCH * 8);
+  uint4 xr[XI];
+  float4 wrg[WI];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      // consecutive lanes take consecutive tokens, so the transposed LDS
+      // writes below fall in different banks
+      const int idx = tid + i * NT;
+      const int t = idx % RT, part = idx / RT;
       const int c = part / 8, m = (part % 8) * 8;
       const int gt = t0 + t, hc = c0 + c;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gt < T && hc < nchunk)
-        v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(gt) * H + hc * 64 + m);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xs[c][m + 2 * i][t] = bf16_to_f32(wv[i] & 0xFFFFu);
-        xs[c][m + 2 * i + 1][t] = bf16_to_f32(wv[i] >> 16);
-      }
+      xr[i] = make_uint4(0, 0, 0, 0);
+      if (idx < XN && gt < T && hc < nchunk)
+        xr[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(gt) * H + hc * 64 + m);
     }
-    for (int idx = tid; idx < kCH * 64 * (kRE / 4); idx += 1024) {  // stage router weights
-      const int row = idx / (kRE / 4), col = (idx % (kRE / 4)) * 4;
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int idx = tid + i * NT;
+      const int row = idx / (RE / 4), col = (idx % (RE / 4)) * 4;
       const int c = row / 64, m = row % 64;
       const int h = (c0 + c) * 64 + m;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + c < nchunk) {
+      if (idx < WN && c0 + c < nchunk) {
         const float* src = wr + static_cast<size_t>(h) * E + e0 + col;
         if (vec_wr && e0 + col + 3 < E) {
           v = *reinterpret_cast<const float4*>(src);
@@ -80,11 +104,42 @@ __global__ __launch_bounds__(1024) void router_scores_kernel(int T, int H, int E
           if (e0 + col + 3 < E) v.w = src[3];
         }
       }
-      *reinterpret_cast<float4*>(&ws[c][m][col]) = v;
+      wrg[i] = v;
     }
-    __syncthreads();
+  };
+  auto store_chunk = [&]() {
 #pragma unroll
-    for (int c = 0; c < kCH; ++c) {
+    for (int i = 0; i < XI; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < XN) {
+        const int t = idx % RT, part = idx / RT;
+        const int c = part / 8, m = (part % 8) * 8;
+        const uint32_t wv[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xs[c][m + 2 * q][t] = bf16_to_f32(wv[q] & 0xFFFFu);
+          xs[c][m + 2 * q + 1][t] = bf16_to_f32(wv[q] >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int idx = tid + i * NT;
+      if (idx < WN) {
+        const int row = idx / (RE / 4), col = (idx % (RE / 4)) * 4;
+        *reinterpret_cast<float4*>(&ws[row / 64][row % 64][col]) = wrg[i];
+      }
+    }
+  };
+
+  load_chunk(0);
+  for (int c0 = 0; c0 < nchunk; c0 += CH) {
+    __syncthreads();  // the previous chunk's reads are done
+    store_chunk();
+    __syncthreads();
+    load_chunk(c0 + CH);  // in flight during the multiply below
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
       if (c0 + c >= nchunk) break;
       float xv[kTW], wv[kEW];
       const float4 xa = *reinterpret_cast<const float4*>(&xs[c][lane][wt * kTW]);
@@ -127,114 +182,127 @@ __global__ __launch_bounds__(1024) void router_scores_kernel(int T, int H, int E
 }
 
 // ---------------------------------------------------------------------------
-// K2: top-k, weights, and the workgroup's histogram with stable local ranks.
-// One wave selects for one token at a time: k rounds of a butterfly arg-max
-// over the token's scores (higher score first, equal scores by lower expert).
-// Then the workgroup's <= 256 slots are ranked within their expert in slot
-// order: a ballot per expert-index bit finds the lanes of a wave that chose
-// the same expert, popcount below the lane gives the rank inside the wave,
-// and the waves add their counts to an LDS histogram one after another.
+// K2: top-k and weights.  A token is served by one 16-lane row of a wave
+// (four tokens per wave); lane r holds the scores of experts r, r+16, r+32...
+// Each of the k rounds takes the lane-local best unselected expert and reduces
+// across the row with four DPP exchanges (row mirror, half-row mirror, quad
+// swaps by 2 and by 1, which pair every lane with every other through the
+// butterfly), ordering by higher score and then lower expert index.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
-__global__ __launch_bounds__(256) void router_topk_kernel(
-    int T, int E, int k, int tpb, const float* __restrict__ logits, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ local_rank, int32_t* __restrict__ partial,
-    uint32_t* __restrict__ status) {
-  __shared__ int sel[256];
-  __shared__ int hist[kMaxE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tbase = blockIdx.x * tpb;
-  for (int e = tid; e < E; e += 256) hist[e] = 0;
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
 
-  const int nc = (E + 63) / 64;
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& be) {
+  const float ov = __int_as_float(dpp<CTRL>(__float_as_int(bv)));
+  const int oe = dpp<CTRL>(be);
+  if (better(ov, oe, bv, be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float sum_step(float v) {
+  return v + __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+
+constexpr int kRowMirror = 0x140, kHalfMirror = 0x141;
+constexpr int kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;  // quad_perm [2,3,0,1] and [1,0,3,2]
+
+template <int VPL>  // scores per lane: E <= 16 * VPL
+__global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
+                                                          const float* __restrict__ logits,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w,
+                                                          uint32_t* __restrict__ bits,
+                                                          uint32_t* __restrict__ status) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int r = lane & 15;
+  const int t = blockIdx.x * 16 + (tid >> 4);
+  const bool tok_ok = t < T;
+  const int tt = tok_ok ? t : 0;  // rows past T work on token 0 and store nothing
+
+  float val[VPL];
   bool saw_nan = false;
-  for (int tt = wave; tt < tpb; tt += 4) {
-    const int t = tbase + tt;
-    if (t >= T) break;
-    float val[kMaxE / 64];
 #pragma unroll
-    for (int c = 0; c < kMaxE / 64; ++c) {
-      const int e = lane + 64 * c;
-      float v = -INFINITY;
-      if (c < nc && e < E) {
-        v = logits[static_cast<size_t>(t) * E + e];
-        if (v != v) {
-          saw_nan = true;
-          v = -INFINITY;
-        }
-      }
-      val[c] = v;
-    }
-    uint32_t taken = 0;
-    float my_v = -INFINITY;  // score of selection number `lane`
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
-#pragma unroll
-      for (int c = 0; c < kMaxE / 64; ++c) {
-        const int e = lane + 64 * c;
-        if (c < nc && e < E && !((taken >> c) & 1u) && better(val[c], e, bv, be)) {
-          bv = val[c];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (better(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (lane == j) my_v = bv;
-      if (lane == 0) {
-        sel[tt * k + j] = be;
-        topk_idx[static_cast<size_t>(t) * k + j] = be;
+  for (int v = 0; v < VPL; ++v) {
+    const int e = r + 16 * v;
+    float s = -INFINITY;
+    if (e < E) {
+      s = logits[static_cast<size_t>(tt) * E + e];
+      if (s != s) {
+        saw_nan = true;
+        s = -INFINITY;
       }
     }
-    // weights: exp(l_j - l_max) / sum over the selected (the softmax
-    // denominator over all experts cancels in the renormalisation)
-    const float top = __shfl(my_v, 0, 64);
-    float ex = (lane < k) ? __expf(my_v - top) : 0.0f;
-    float den = ex;
+    val[v] = s;
+  }
+  uint64_t taken = 0;
+  float sel_v[2] = {-INFINITY, -INFINITY};  // selections r and r + 16 of this token
+  int sel_e[2] = {0, 0};
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
-    if (lane < k) topk_w[static_cast<size_t>(t) * k + lane] = ex / den;
+    for (int v = 0; v < VPL; ++v) {
+      const int e = r + 16 * v;
+      if (e < E && !((taken >> v) & 1ull) && better(val[v], e, bv, be)) {
+        bv = val[v];
+        be = e;
+      }
+    }
+    argmax_step<kRowMirror>(bv, be);
+    argmax_step<kHalfMirror>(bv, be);
+    argmax_step<kQuadSwap2>(bv, be);
+    argmax_step<kQuadSwap1>(bv, be);
+    if ((be & 15) == r) taken |= 1ull << (be >> 4);
+    if (j == r) {
+      sel_v[0] = bv;
+      sel_e[0] = be;
+    }
+    if (j == r + 16) {
+      sel_v[1] = bv;
+      sel_e[1] = be;
+    }
   }
-  if (saw_nan) status_set(status, MOE_STATUS_NAN_LOGIT);
-  __syncthreads();
-
-  const int nslot = min(tpb, T - tbase) * k;
-  const bool valid = tid < nslot;
-  const int e = valid ? sel[tid] : 0;
-  uint64_t match = __ballot(valid);
-  for (int b = 0; (1 << b) < E; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t bb = __ballot(valid && bit);
-    match &= bit ? bb : ~bb;
+  // weights: exp(l_j - l_max) / sum over the selected (the softmax
+  // denominator over all experts cancels in the renormalisation)
+  const float top = __int_as_float(__shfl(__float_as_int(sel_v[0]), lane & ~15, 64));
+  float ex[2];
+  float den = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = r + 16 * q;
+    ex[q] = (j < k) ? __expf(sel_v[q] - top) : 0.0f;
+    den += ex[q];
   }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int rank_in_wave = __popcll(match & below);
-  const int cnt_in_wave = __popcll(match);
-  int rank = 0;
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w && valid) rank = hist[e] + rank_in_wave;
-    __syncthreads();
-    if (wave == w && valid && rank_in_wave == 0) hist[e] += cnt_in_wave;
-    __syncthreads();
+  den = sum_step<kRowMirror>(den);
+  den = sum_step<kHalfMirror>(den);
+  den = sum_step<kQuadSwap2>(den);
+  den = sum_step<kQuadSwap1>(den);
+  if (tok_ok) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int j = r + 16 * q;
+      if (j < k) {
+        topk_idx[static_cast<size_t>(t) * k + j] = sel_e[q];
+        topk_w[static_cast<size_t>(t) * k + j] = ex[q] / den;
+        atomicOr(&bits[static_cast<size_t>(t >> 5) * E + sel_e[q]], 1u << (t & 31));
+      }
+    }
   }
-  if (valid) local_rank[static_cast<size_t>(tbase) * k + tid] = rank;
-  for (int x = tid; x < E; x += 256) partial[static_cast<size_t>(blockIdx.x) * E + x] = hist[x];
+  if (saw_nan && tok_ok) status_set(status, MOE_STATUS_NAN_LOGIT);
 }
 
 // ---------------------------------------------------------------------------
-// K3: one workgroup: per-expert totals and per-(workgroup, expert) bases, the
-// exclusive scan into offsets, the block map, and the stable scatter.
+// K3: one workgroup of 1024 threads.
 // ---------------------------------------------------------------------------
 __device__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -263,40 +331,47 @@ __device__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(
-    int T, int E, int k, int n_shared, int tile_m_max, int tile_gran, int nwg, int tpb,
-    int32_t* __restrict__ partial, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ local_rank,
+    int T, int E, int k, int n_shared, int tile_m_max, int tile_gran,
+    const uint32_t* __restrict__ bits, int32_t* __restrict__ pref, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, const int32_t* __restrict__ topk_idx,
     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos, int32_t* __restrict__ blocks,
     int32_t* __restrict__ n_blocks, int max_blocks, uint32_t* __restrict__ status) {
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_bstart[kMaxE + 2];
   __shared__ int s_cnt[kMaxE + 1];
+  __shared__ int s_part[1024];
   __shared__ int tmp[17];
   const int tid = threadIdx.x;
   const int S = T * k;
+  const int W = (T + 31) / 32;
 
-  // per expert: running sum over the routing workgroups (in workgroup order)
+  // Per-expert prefix popcounts over the token words: thread (e, q) of the
+  // tpe threads of expert e counts words [q*W/tpe, (q+1)*W/tpe).
+  const int tpe = max(1, 1024 / E);
+  const int e = tid % E, q = tid / E;
+  const bool scanner = tid < E * tpe;
+  const int w0 = scanner ? static_cast<int>(static_cast<long long>(q) * W / tpe) : 0;
+  const int w1 = scanner ? static_cast<int>(static_cast<long long>(q + 1) * W / tpe) : 0;
+  int part = 0;
+  for (int w = w0; w < w1; ++w) part += __popc(bits[static_cast<size_t>(w) * E + e]);
+  s_part[tid] = part;
+  __syncthreads();
   int cnt = 0;
-  if (tid < E) {
-    int g = 0;
-    for (; g + 4 <= nwg; g += 4) {
-      int c[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) c[u] = partial[static_cast<size_t>(g + u) * E + tid];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        partial[static_cast<size_t>(g + u) * E + tid] = cnt;
-        cnt += c[u];
-      }
+  if (scanner) {
+    int base = 0;
+    for (int p = 0; p < tpe; ++p) {
+      const int v = s_part[p * E + e];
+      if (p < q) base += v;
+      cnt += v;
     }
-    for (; g < nwg; ++g) {
-      const int c = partial[static_cast<size_t>(g) * E + tid];
-      partial[static_cast<size_t>(g) * E + tid] = cnt;
-      cnt += c;
+    int run = base;
+    for (int w = w0; w < w1; ++w) {
+      pref[static_cast<size_t>(w) * E + e] = run;
+      run += __popc(bits[static_cast<size_t>(w) * E + e]);
     }
   }
   int total = 0;
-  const int off = block_exclusive_scan(tid < E ? cnt : 0, tmp, &total);
+  const int off = block_exclusive_scan((tid < E) ? cnt : 0, tmp, &total);
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = off;
@@ -307,6 +382,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     offsets[E] = total;
     s_off[E] = S;
     s_cnt[E] = n_shared ? T : 0;
+    if (total != S) status_set(status, MOE_STATUS_BAD_INDEX);
   }
   __syncthreads();
 
@@ -337,30 +413,51 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     const int c = s_cnt[g];
     const int ng = s_bstart[g + 1] - s_bstart[g];
     const int i = b - s_bstart[g];
-    const int base = c / ng, rem = c % ng;
-    const int rows = base + (i < rem ? 1 : 0);
-    const int first = (g < E ? s_off[g] : S) + i * base + min(i, rem);
-    const int tallest = base + (rem > 0 ? 1 : 0);
+    const int bs = c / ng, rem = c % ng;
+    const int rows = bs + (i < rem ? 1 : 0);
+    const int first = (g < E ? s_off[g] : S) + i * bs + min(i, rem);
+    const int tallest = bs + (rem > 0 ? 1 : 0);
     const int tm = (tallest + tile_gran - 1) / tile_gran * tile_gran;
     reinterpret_cast<int4*>(blocks)[b] = make_int4(g, first, rows, tm);
   }
 
-  // stable scatter: row = offset of the expert + slots of earlier routing
-  // workgroups + rank inside this slot's workgroup
-  for (int s = tid; s < S; s += 1024) {
-    const int e = topk_idx[s];
-    if (e < 0 || e >= E) {
-      status_set(status, MOE_STATUS_BAD_INDEX);
-      continue;
+  // stable scatter: row = expert offset + tokens before t that chose e; four
+  // slots per thread per pass so their loads overlap
+  for (int s0 = tid; s0 < S; s0 += 4 * 1024) {
+    int ex[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u * 1024;
+      ex[u] = (s < S) ? topk_idx[s] : 0;
     }
-    const int g = (s / k) / tpb;
-    const int pos = s_off[e] + partial[static_cast<size_t>(g) * E + e] + local_rank[s];
-    if (pos < 0 || pos >= S) {
-      status_set(status, MOE_STATUS_BAD_INDEX);
-      continue;
+    uint32_t wbits[4];
+    int wpref[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u * 1024;
+      const int t = (s < S) ? s / k : 0;
+      const int e = min(max(ex[u], 0), E - 1);
+      const size_t wi = static_cast<size_t>(t >> 5) * E + e;
+      wbits[u] = bits[wi];
+      wpref[u] = pref[wi];
     }
-    sorted_slot[pos] = s;
-    slot_pos[s] = pos;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u * 1024;
+      if (s >= S) continue;
+      if (ex[u] < 0 || ex[u] >= E) {
+        status_set(status, MOE_STATUS_BAD_INDEX);
+        continue;
+      }
+      const int t = s / k;
+      const int pos = s_off[ex[u]] + wpref[u] + __popc(wbits[u] & ((1u << (t & 31)) - 1u));
+      if (pos < 0 || pos >= S) {
+        status_set(status, MOE_STATUS_BAD_INDEX);
+        continue;
+      }
+      sorted_slot[pos] = s;
+      slot_pos[s] = pos;
+    }
   }
 }
 
@@ -368,19 +465,29 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
 hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, const float* bias,
                         const RouteBuffers& rb, hipStream_t stream) {
   const int T = d.T, E = d.E, k = d.k;
-  dim3 g1((T + kRT - 1) / kRT, (E + kRE - 1) / kRE);
+  const int nbits = ((T + 31) / 32) * E;
   // 16-byte router loads only when every row start is 16-byte aligned
   const int vec_wr = (E % 4 == 0) && (reinterpret_cast<uintptr_t>(wr) % 16 == 0);
-  hipLaunchKernelGGL(router_scores_kernel, g1, dim3(1024), 0, stream, T, d.H, E, vec_wr, x, wr,
-                     bias, rb.logits, rb.status);
-  const int tpb = route_tokens_per_wg(k);
-  const int nwg = (T + tpb - 1) / tpb;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(nwg), dim3(256), 0, stream, T, E, k, tpb,
-                     rb.logits, rb.topk_idx, rb.topk_w, rb.local_rank, rb.partial, rb.status);
+  if (T >= 1024) {  // 32 x 32 tiles, 16 waves
+    const dim3 g1((T + 31) / 32, (E + 31) / 32);
+    hipLaunchKernelGGL((router_scores_kernel<4, 4, 2>), g1, dim3(1024), 0, stream, T, d.H, E,
+                       vec_wr, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
+  } else {  // 16 x 16 tiles, 4 waves: more workgroups for short batches
+    const dim3 g1((T + 15) / 16, (E + 15) / 16);
+    hipLaunchKernelGGL((router_scores_kernel<2, 2, 4>), g1, dim3(256), 0, stream, T, d.H, E,
+                       vec_wr, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
+  }
+  const dim3 g2((T + 15) / 16);
+  if (E <= 256)
+    hipLaunchKernelGGL((router_topk_kernel<16>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
+                       rb.topk_idx, rb.topk_w, rb.bits, rb.status);
+  else
+    hipLaunchKernelGGL((router_topk_kernel<64>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
+                       rb.topk_idx, rb.topk_w, rb.bits, rb.status);
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, T, E, k, d.n_shared,
-                     d.tile_m_max, d.tile_gran, nwg, tpb, rb.partial, rb.counts, rb.offsets,
-                     rb.topk_idx, rb.local_rank, rb.sorted_slot, rb.slot_pos, rb.blocks,
-                     rb.n_blocks, rb.max_blocks, rb.status);
+                     d.tile_m_max, d.tile_gran, rb.bits, rb.pref, rb.counts, rb.offsets,
+                     rb.topk_idx, rb.sorted_slot, rb.slot_pos, rb.blocks, rb.n_blocks,
+                     rb.max_blocks, rb.status);
   return hipGetLastError();
 }
 
