@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_prefill512.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_prefill512.txt")
+DOMINANT = "w4_gemm_small_kernel<true>"   # the gate/up GEMM of the 512-token workload
 # Tile height bound per workload: uniform routing at 512 tokens gives every
 # expert 7-27 rows, so 32-row tiles cover them and the shared expert's 512
 # rows in 16 blocks; the skewed 2048-token batch has groups of up to ~2000
@@ -50,6 +51,9 @@ def parse():
                    help="also run one plain device copy of this size (counter calibration)")
     p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1"], default=None,
                    help="time a single workload (profiling runs)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                   help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                        "'--only prefill512 --calib-copy-mb N' into the stored traffic record")
     return p.parse_args()
 
 
@@ -161,6 +165,39 @@ def traffic_record():
     return rec.get("bytes_per_launch")
 
 
+def _pmc_rows(d, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def write_traffic(fetch_dir, write_dir, calib_bytes):
+    """HBM bytes per launch of the dominant kernel, scaled by the same counters'
+    reading for a plain device copy of calib_bytes (read once, written once)."""
+    rec = {"kernel": DOMINANT, "kernel_source_hash": kernel_source_hash()}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(d, counter)
+        kern = [v for _, n, v in rows if DOMINANT in n]
+        copy = [v for _, n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        kib = sorted(kern)[len(kern) // 2]           # median over launches, KiB
+        calib_kib = max(copy)                        # the large calibration copy
+        factor = (calib_bytes / 1024.0) / calib_kib
+        rec[key + "_kib_raw"] = kib
+        rec[key + "_calib_kib_raw"] = calib_kib
+        rec[key + "_scale"] = factor
+        rec[key + "_bytes"] = kib * 1024.0 * factor
+    rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
 def cpu_baseline(name, budget_tokens):
     """The oracle, untuned, on the host cores: route + layer for a sample of the batch."""
     import oracle
@@ -179,6 +216,9 @@ def cpu_baseline(name, budget_tokens):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(*args.traffic_from, calib_bytes=(args.calib_copy_mb or 256) << 20)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the layer shards by token with no exchange; see the design notes)", file=sys.stderr)
@@ -267,7 +307,7 @@ def main():
                    "experts": 256, "top_k": 8, "shared_experts": 1, "expert_intermediate": 512,
                    "weights": "4-bit codes, bf16 scale+bias per 64", "weight_copies": args.copies,
                    "tile_m_max": args.tile_m_max or TILE_M_MAX[main_name]},
-        "roofline": {"bound": "hbm", "kernel": "w4_grouped_gemm_kernel<gate_up>",
+        "roofline": {"bound": "hbm", "kernel": DOMINANT,
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(),
                      "algorithmic_bytes": work["bytes_gate_up"],

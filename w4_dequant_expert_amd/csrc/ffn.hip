@@ -253,21 +253,19 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
 
 // ---------------------------------------------------------------------------
 // Tall-tile kernel: blocks of 48..128 rows.  Four waves, four slices each,
-// every wave holding all 128 tile rows of accumulators.
+// every wave holding all of the block's tile rows of accumulators.  The block
+// body is instantiated per tile height (MT = 3..8 row tiles of 16), so its
+// step loop has no per-row-tile branches, and the weights of step s+1 are
+// rebuilt between the MFMAs of step s (two B buffers): the VALU work of the
+// reconstruction overlaps the matrix units instead of preceding them.
 // ---------------------------------------------------------------------------
-template <int M_MAX, bool GATE_UP>
-__global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
-                                                           const uint16_t* __restrict__ src,
-                                                           uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][M_MAX * kLDA];
-  __shared__ int s_tok[M_MAX];
-  constexpr int AV = M_MAX / 16;  // 16-byte A chunks staged per thread per step
+constexpr int kTallM = 128;
 
-  BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi)) return;
-  if (bi.tm <= kSmallM) return;  // a short block: the small-tile kernel owns it
-  if (!block_valid<GATE_UP>(a, bi, M_MAX)) return;
-
+template <int MT, bool GATE_UP>
+__device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& bi,
+                                           const uint16_t* __restrict__ src,
+                                           uint16_t* __restrict__ out,
+                                           uint16_t (*As)[kTallM * kLDA], const int* s_tok) {
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int nk = pack_steps(K);
@@ -275,7 +273,6 @@ __global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
   const int wave = uniform(tid >> 6);
   const int n = lane & 15;
   const int lk = (lane >> 4) * 32;
-  const int mtiles = bi.tm >> 4;
   const int row0 = bi.row0, rows = bi.rows;
 
   const int c_first = bi.nt * 16 + wave * 4;
@@ -283,37 +280,29 @@ __global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
   const uint8_t* sbase = bi.P + static_cast<size_t>(active ? c_first : 0) * nk * kPackBlock;
   const size_t sstride = static_cast<size_t>(nk) * kPackBlock;
 
-  if (GATE_UP) {
-    block_tokens(a, bi, s_tok);
-    __syncthreads();
-  }
-
+  // A staging: chunk i of this thread is tile row (tid + 256 i) / 16 and
+  // 16-byte column tid % 16; rows past the block read row 0 and are zeroed.
   const int ac = tid & 15;
-  const uint16_t* arow[AV];
-  bool a_ok[AV];
+  int arow[MT];  // source row (token for gate/up, h row for down); -1 = pad
 #pragma unroll
-  for (int i = 0; i < AV; ++i) {
+  for (int i = 0; i < MT; ++i) {
     const int m = (tid + 256 * i) >> 4;
-    a_ok[i] = m < rows;
-    if (GATE_UP) {
-      const int tok = (m < bi.tm) ? s_tok[m] : -1;
-      a_ok[i] = a_ok[i] && tok >= 0;
-      arow[i] = src + static_cast<size_t>(a_ok[i] ? tok : 0) * K;
-    } else {
-      arow[i] = src + static_cast<size_t>(row0 + (a_ok[i] ? m : 0)) * K;
-    }
+    int r = -1;
+    if (m < rows) r = GATE_UP ? s_tok[m] : row0 + m;
+    arow[i] = r;
   }
-  auto load_a = [&](int s, uint4 (&ar)[AV]) {
+  auto load_a = [&](int s, uint4 (&ar)[MT]) {
+    const int kk = min(s * kKS + ac * 8, K - 8);
 #pragma unroll
-    for (int i = 0; i < AV; ++i)
-      ar[i] = *reinterpret_cast<const uint4*>(arow[i] + min(s * kKS + ac * 8, K - 8));
+    for (int i = 0; i < MT; ++i)
+      ar[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(max(arow[i], 0)) * K + kk);
   };
-  auto store_a = [&](int buf, uint4 (&ar)[AV], int s) {
+  auto store_a = [&](int buf, uint4 (&ar)[MT], int s) {
     const bool kin = s < nk && s * kKS + ac * 8 < K;
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int m = (tid + 256 * i) >> 4;  // always < M_MAX: unconditional store
-      const uint4 v = (a_ok[i] && kin) ? ar[i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < MT; ++i) {
+      const int m = (tid + 256 * i) >> 4;
+      const uint4 v = (arow[i] >= 0 && kin) ? ar[i] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&As[buf][m * kLDA + ac * 8]) = v;
     }
   };
@@ -322,59 +311,67 @@ __global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) load_slice(sbase + ns * sstride + off, lane, o[ns]);
   };
+  // rebuild word w (0..15: slice w/4, 32-bit word w%4) of a code slot
+  auto rebuild_word = [&](const SliceOps (&o)[4], bf16x8 (&b)[4][4], int w) {
+    const SliceOps& so = o[w >> 2];
+    const float sc = bf16_to_f32(so.sb & 0xFFFFu), bi2 = bf16_to_f32(so.sb >> 16);
+    const uint32_t q = (w & 3) == 0 ? so.q.x : (w & 3) == 1 ? so.q.y : (w & 3) == 2 ? so.q.z : so.q.w;
+    b[w >> 2][w & 3] = as_bf16x8(dequant8(q, sc, bi2));
+  };
 
-  f32x4 acc[M_MAX / 16][4];
+  f32x4 acc[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < M_MAX / 16; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int s, SliceOps (&o)[4], int buf, uint4 (&ar)[AV]) {
-    bf16x8 bfr[4][4];
+  constexpr int WPER = (16 + MT - 1) / MT;  // rebuilt words per row tile
+  // One step: MFMAs of step s on bcur; in between, rebuild step s+1 (slot
+  // cnext) into bnext; then refill cnext with the codes of step s+3.
+  auto step = [&](int s, bf16x8 (&bcur)[4][4], bf16x8 (&bnext)[4][4], SliceOps (&cnext)[4],
+                  int buf, uint4 (&ar)[MT]) {
     if (active) {
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) rebuild_slice(o[ns], bfr[ns]);
-    }
-    load_codes(s + 2, o);
-    if (active) {
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk];
+        bf16x8 af[4];
 #pragma unroll
-      for (int mt = 0; mt < M_MAX / 16; ++mt) {
-        if (mt < mtiles) {
-          const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk];
-          bf16x8 af[4];
+        for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
+        for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-          for (int ns = 0; ns < 4; ++ns)
+          for (int j = 0; j < 4; ++j)
+            acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bcur[ns][j], acc[mt][ns], 0, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[mt][ns] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfr[ns][j], acc[mt][ns], 0, 0, 0);
-        }
+        for (int w = mt * WPER; w < (mt + 1) * WPER && w < 16; ++w) rebuild_word(cnext, bnext, w);
       }
     }
+    load_codes(s + 3, cnext);
     store_a(buf ^ 1, ar, s + 1);
     load_a(s + 2, ar);
     __syncthreads();
   };
 
   SliceOps c0[4], c1[4];
+  bf16x8 b0[4][4], b1[4][4];
   load_codes(0, c0);
   load_codes(1, c1);
-  uint4 ar[AV];
+  uint4 ar[MT];
   load_a(0, ar);
   store_a(0, ar, 0);
   load_a(1, ar);
+#pragma unroll
+  for (int w = 0; w < 16; ++w) rebuild_word(c0, b0, w);
+  load_codes(2, c0);
   __syncthreads();
   for (int s = 0; s < nk; s += 2) {
-    step(s, c0, 0, ar);
-    if (s + 1 < nk) step(s + 1, c1, 1, ar);
+    step(s, b0, b1, c1, 0, ar);
+    if (s + 1 < nk) step(s + 1, b1, b0, c0, 1, ar);
   }
   if (!active) return;
 
 #pragma unroll
-  for (int mt = 0; mt < M_MAX / 16; ++mt) {
-    if (mt >= mtiles) break;
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + (lane >> 4) * 4 + i;
@@ -397,6 +394,31 @@ __global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
   }
 }
 
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
+                                                           const uint16_t* __restrict__ src,
+                                                           uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTallM * kLDA];
+  __shared__ int s_tok[kTallM];
+
+  BlockInfo bi;
+  if (!block_info<GATE_UP>(a, bi)) return;
+  if (bi.tm <= kSmallM) return;  // a short block: the small-tile kernel owns it
+  if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
+  if (GATE_UP) {
+    block_tokens(a, bi, s_tok);
+    __syncthreads();
+  }
+  switch (bi.tm >> 4) {
+    case 3: tall_block<3, GATE_UP>(a, bi, src, out, As, s_tok); break;
+    case 4: tall_block<4, GATE_UP>(a, bi, src, out, As, s_tok); break;
+    case 5: tall_block<5, GATE_UP>(a, bi, src, out, As, s_tok); break;
+    case 6: tall_block<6, GATE_UP>(a, bi, src, out, As, s_tok); break;
+    case 7: tall_block<7, GATE_UP>(a, bi, src, out, As, s_tok); break;
+    default: tall_block<8, GATE_UP>(a, bi, src, out, As, s_tok); break;
+  }
+}
+
 // Tall-tile kernel variant for a tile height bound (0: no tile exceeds kSmallM).
 int gemm_m_max_for(int tile_m_max) { return tile_m_max <= kSmallM ? 0 : 128; }
 
@@ -407,7 +429,7 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
   const dim3 grid(static_cast<unsigned>(a.max_blocks) * ntiles);
   hipLaunchKernelGGL((w4_gemm_small_kernel<GATE_UP>), grid, dim3(512), 0, stream, a, src, out);
   if (m_max)
-    hipLaunchKernelGGL((w4_gemm_tall_kernel<128, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
+    hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
   return hipGetLastError();
 }
 
