@@ -11,7 +11,8 @@ router) are rotated so that no call finds the previous call's weights in the
 
 Prints one JSON line.  Also measured (reported under "extra"): the
 2048-token Zipf-skewed prefill (MFMA fraction of the two GEMMs) and batch-1
-decode (HBM fraction of the two GEMMs), and the CPU oracle on the host cores.
+decode (HBM fraction of the two GEMMs; its launch-bound steps are timed from
+HIP graph replays), and the CPU oracle on the host cores.
 """
 
 from __future__ import annotations
@@ -154,6 +155,78 @@ def time_workload(wl, steps, warmup, fresh_tokens=None):
     return wall, dict(route_ms=stage[0], gate_up_ms=stage[1], down_ms=stage[2], combine_ms=stage[3])
 
 
+def graph_ms(fn, n_inner, replays=5):
+    """Device time per call of fn(i), i = 0..n_inner-1, captured once in a HIP
+    graph and replayed: launch-bound calls then run back to back."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n_inner):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_inner):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * n_inner)
+
+
+def decode_leg(copies=40):
+    """Batch-1 decode: whole steps and each stage timed from HIP graph replays
+    (40 steps per graph, each with its own weight copy and fresh token)."""
+    import numpy as np
+    import torch
+
+    from synth import make_tokens
+    wl = Workload("decode1", copies)
+    fresh = [torch.from_numpy(make_tokens(1, 2048, 4, t0=i).view(np.int16)).to("cuda")
+             for i in range(copies)]
+    for i in range(5):
+        wl.step(i, x=fresh[i])
+    # eager steps (host launch overhead included) for reference
+    w_eager, _ = time_workload(wl, 200, 20, fresh)
+    step_ms = graph_ms(lambda i: wl.step(i, x=fresh[i]), copies)
+    L = wl.layer
+    d = L.dims(1)
+    x0 = fresh[0]
+    L.route(x0)
+
+    def route(i):
+        L.w_router = wl.copies[i][2]
+        L.route(fresh[i])
+    route_ms = graph_ms(route, copies)
+    L.w_router = wl.copies[0][2]
+    L.route(x0)
+    gu_ms = graph_ms(lambda i: L.gate_up(d, x0, wl.copies[i][0], wl.copies[i][1]), copies)
+    dn_ms = graph_ms(lambda i: L.down(d, wl.copies[i][0], wl.copies[i][1]), copies)
+    cb_ms = graph_ms(lambda i: L.combine(d, wl.y), copies)
+    wk = wl.work()
+    g_s = (gu_ms + dn_ms) * 1e-3
+    out = dict(
+        tokens_per_s=1.0 / (step_ms * 1e-3), ms_per_step=step_ms, timing="hip graph replay",
+        eager_tokens_per_s=200 / w_eager,
+        route_ms=round(route_ms, 5), gate_up_ms=round(gu_ms, 5), down_ms=round(dn_ms, 5),
+        combine_ms=round(cb_ms, 5),
+        gate_up_hbm_gbs=wk["bytes_gate_up"] / (gu_ms * 1e-3) / 1e9,
+        down_hbm_gbs=wk["bytes_down"] / (dn_ms * 1e-3) / 1e9,
+        gemm_hbm_gbs=(wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9,
+        gemm_frac_hbm=(wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9 / PEAK_HBM_GBS,
+        gemm_bytes=wk["bytes_gate_up"] + wk["bytes_down"],
+        bytes_per_token=wk["bytes_layer"], weight_copies=copies)
+    del wl
+    return out
+
+
 def traffic_record():
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -240,13 +313,11 @@ def main():
 
     extra = {}
     main_name = args.only or "prefill512"
+    if main_name == "decode1":  # profiling runs of the decode leg alone
+        print(json.dumps({"decode1": decode_leg(40)}))
+        return
     wl = Workload(main_name, args.copies, args.tile_m_max)
-    fresh = None
-    if main_name == "decode1":
-        from synth import make_tokens
-        fresh = [torch.from_numpy(make_tokens(1, 2048, 4, t0=i).view(np.int16)).to("cuda")
-                 for i in range(256)]
-    wall, stages = time_workload(wl, args.steps, args.warmup, fresh)
+    wall, stages = time_workload(wl, args.steps, args.warmup)
     work = wl.work()
     ms = wall / args.steps * 1e3
     tok_s = wl.T * args.steps / wall
@@ -275,19 +346,7 @@ def main():
             touched_experts=wk2["touched"])
         del wl2
         torch.cuda.empty_cache()
-        wl5 = Workload("decode1", 40, args.tile_m_max)
-        from synth import make_tokens
-        fresh = [torch.from_numpy(make_tokens(1, 2048, 4, t0=i).view(np.int16)).to("cuda")
-                 for i in range(200)]
-        w5, st5 = time_workload(wl5, 200, 20, fresh)
-        wk5 = wl5.work()
-        g5 = (st5["gate_up_ms"] + st5["down_ms"]) * 1e-3
-        extra["decode1"] = dict(
-            tokens_per_s=200 / w5, **{k: round(v, 5) for k, v in st5.items()},
-            gemm_hbm_gbs=(wk5["bytes_gate_up"] + wk5["bytes_down"]) / g5 / 1e9,
-            gemm_frac_hbm=(wk5["bytes_gate_up"] + wk5["bytes_down"]) / g5 / 1e9 / PEAK_HBM_GBS,
-            bytes_per_token=wk5["bytes_layer"], weight_copies=40)
-        del wl5
+        extra["decode1"] = decode_leg(40)
         torch.cuda.empty_cache()
 
     out = {

@@ -277,12 +277,32 @@ def test_deterministic_and_chunk_independent(full_banks):
     assert np.array_equal(np.concatenate(ys), y_all)
 
 
+# ----------------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T", [2, 5, 16, 17, 64, 1024])
+def test_routing_batch_sizes(full_banks, T):
+    """Each router-score kernel variant (short batches up to 16 tokens, 16- and
+    32-token tiles) and the scan against the oracle, with a logit bias."""
+    note(f"case routing T={T}")
+    c = build_config("prefill2048_zipf", T=T, with_weights=False)
+    sh = c["shape"]
+    _, _, routed_dev, shared_dev = full_banks
+    layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, routed_dev, shared_dev, c["wr"],
+                         c["bias"], T_max=T, tile_m_max=128, export_logits=True)
+    layer.route(dev(c["x"]))
+    torch.cuda.synchronize()
+    r = oracle.route(c["x"], c["wr"], c["bias"], sh.k, sh.n_shared, 128, 16, NTHREADS)
+    check_routing(layer.rt.host(), r, f"T={T}")
+
+
 # ----------------------------------------------------------------------------- odd shapes
 
 @pytest.mark.parametrize("H,I,E,k,n_shared,T", [
     (192, 64, 5, 5, 1, 33),     # K tails (H % 128 = 64, I = 64), E < 32, k = E
     (128, 128, 40, 1, 0, 70),   # no shared expert, k = 1
     (256, 192, 33, 3, 1, 9),    # E not a multiple of 32, I % 128 = 64
+    (1088, 320, 24, 4, 1, 5),   # short batch: inputs split over two waves, K tails in both GEMMs
+    (2112, 64, 16, 2, 1, 3),    # short batch: a wave with more steps than one load chunk
 ])
 def test_odd_shapes(H, I, E, k, n_shared, T):
     note(f"case odd shape H={H} I={I} E={E} k={k} shared={n_shared} T={T}")

@@ -419,12 +419,168 @@ __global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short-batch kernel (every block at most 16 rows: decode and batches of up
+// to 16 tokens).  The weight stream is spread over the whole chip: a
+// workgroup of four waves covers 4/KS slices of one block, and each wave
+// handles one slice over 1/KS of the input steps.  A wave issues all loads of
+// a chunk of steps (codes, scale/bias words and its activation fragments,
+// read straight from memory in the MFMA layout) before its first multiply;
+// the KS partial sums of a slice are then added in LDS in wave order.
+// ---------------------------------------------------------------------------
+constexpr int kGemvRows = 16;   // rows per block this kernel accepts
+constexpr int kGemvChunk = 4;   // steps whose loads are in flight together
+
+template <int KS, bool GATE_UP>
+__global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t* __restrict__ src,
+                                                      uint16_t* __restrict__ out) {
+  constexpr int SPW = 4 / KS;  // slices per workgroup
+  __shared__ f32x4 red[4][64];
+
+  const int K = GATE_UP ? a.H : a.I;
+  const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
+  const int ntiles = (nslices + SPW - 1) / SPW;
+  const int bid = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+  const int nblk = min(*a.n_blocks, a.max_blocks);
+  if (bid >= nblk) return;
+  BlockInfo bi;
+  {
+    const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
+    bi.G = blk.x;
+    bi.row0 = blk.y;
+    bi.rows = blk.z;
+    bi.tm = blk.w;
+    bi.nt = 0;
+  }
+  if (bi.rows > kGemvRows) {  // the host launches this kernel only when T <= 16
+    if (threadIdx.x == 0) status_set(a.status, MOE_STATUS_BAD_INDEX);
+    return;
+  }
+  if (!block_valid<GATE_UP>(a, bi, 1 << 30)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int ws = wave / KS, wk = wave % KS;
+  const bool c_ok = tile * SPW + ws < nslices;
+  const int c = min(tile * SPW + ws, nslices - 1);  // a clamped slice computes, never stores
+  const int nk = pack_steps(K);
+  const int s_begin = wk * nk / KS, s_end = (wk + 1) * nk / KS;
+  const uint8_t* sbase = bi.P + static_cast<size_t>(c) * nk * kPackBlock;
+
+  // source row of MFMA row r = lane % 16 (-1: no row); this load goes first,
+  // so that waiting for it leaves the weight loads below in flight
+  const int r = lane & 15;
+  const int Sk = a.T * a.k;
+  const int rr = bi.row0 + min(r, bi.rows - 1);
+  int srow = GATE_UP ? ((rr < Sk) ? a.sorted_slot[rr] : rr) : rr;
+
+  auto load_w = [&](int s0, SliceOps (&o)[kGemvChunk]) {
+#pragma unroll
+    for (int u = 0; u < kGemvChunk; ++u)
+      load_slice(sbase + static_cast<size_t>(min(s0 + u, max(s_end - 1, 0))) * kPackBlock, lane, o[u]);
+  };
+  SliceOps o0[kGemvChunk];
+  load_w(s_begin, o0);
+
+  if (GATE_UP) {
+    srow = (rr < Sk) ? srow / a.k : rr - Sk;
+    if (srow < 0 || srow >= a.T) {
+      status_set(a.status, MOE_STATUS_BAD_INDEX);
+      srow = 0;
+    }
+  }
+  // Rows past the block read the block's last row: an MFMA row only reaches
+  // its own output row, and those are never stored.
+  const uint16_t* arow = src + static_cast<size_t>(srow) * K;
+  const int kq = (lane >> 4) * 32;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto chunk = [&](int s0, const SliceOps (&o)[kGemvChunk]) {
+    uint4 av[kGemvChunk][4];
+#pragma unroll
+    for (int u = 0; u < kGemvChunk; ++u) {
+      const int s = min(s0 + u, s_end - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        av[u][j] = *reinterpret_cast<const uint4*>(arow + min(s * kKS + kq + 8 * j, K - 8));
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvChunk; ++u) {
+      // Steps past the wave's range and inputs past K multiply zeros (the
+      // mask is opaque to the compiler, so the loads above stay unconditional
+      // and their wait counts exact); the weights there are finite.
+      bf16x8 b[4];
+      rebuild_slice(o[u], b);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + kq + 8 * j < K) ? ~0u : 0u;
+        asm("" : "+v"(mk));
+        const uint4 v = make_uint4(av[u][j].x & mk, av[u][j].y & mk, av[u][j].z & mk, av[u][j].w & mk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v), b[j], acc, 0, 0, 0);
+      }
+    }
+  };
+  // the first chunk is peeled, so its weight loads (issued above) are not
+  // loop-carried and nothing waits for them before the activation loads
+  if (s_begin < s_end) chunk(s_begin, o0);
+  for (int s0 = s_begin + kGemvChunk; s0 < s_end; s0 += kGemvChunk) {
+    SliceOps o1[kGemvChunk];
+    load_w(s0, o1);
+    chunk(s0, o1);
+  }
+
+  if (KS > 1) {
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int q = 1; q < KS; ++q) acc += red[wave + q][lane];
+  }
+  if (!c_ok) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = (lane >> 4) * 4 + i;
+    const int n = lane & 15;
+    const size_t row = static_cast<size_t>(bi.row0 + m);
+    const float v = acc[i];
+    if (GATE_UP) {
+      const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
+      if (n < 8 && m < bi.rows) {
+        const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+        out[row * a.I + c * 8 + n] = f32_to_bf16(hv);
+      }
+    } else if (m < bi.rows) {
+      out[row * a.H + c * 16 + n] = f32_to_bf16(v);
+    }
+  }
+}
+
+template <bool GATE_UP>
+static hipError_t launch_gemv(const GemmArgs& a, const uint16_t* src, uint16_t* out,
+                              hipStream_t stream) {
+  const int K = GATE_UP ? a.H : a.I;
+  const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
+  const int nk = pack_steps(K);
+  // about four steps per wave: split the inputs of a slice over up to four waves
+  const int ks = nk >= 16 ? 4 : nk >= 8 ? 2 : 1;
+  const int spw = 4 / ks;
+  const dim3 grid(static_cast<unsigned>(a.max_blocks) * ((nslices + spw - 1) / spw));
+  if (ks == 4)
+    hipLaunchKernelGGL((w4_gemv_kernel<4, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
+  else if (ks == 2)
+    hipLaunchKernelGGL((w4_gemv_kernel<2, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
+  else
+    hipLaunchKernelGGL((w4_gemv_kernel<1, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
+  return hipGetLastError();
+}
+
 // Tall-tile kernel variant for a tile height bound (0: no tile exceeds kSmallM).
 int gemm_m_max_for(int tile_m_max) { return tile_m_max <= kSmallM ? 0 : 128; }
 
 template <bool GATE_UP>
 static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src, uint16_t* out,
                               hipStream_t stream) {
+  if (a.T <= kGemvRows) return launch_gemv<GATE_UP>(a, src, out, stream);
   const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
   const dim3 grid(static_cast<unsigned>(a.max_blocks) * ntiles);
   hipLaunchKernelGGL((w4_gemm_small_kernel<GATE_UP>), grid, dim3(512), 0, stream, a, src, out);
@@ -458,27 +614,48 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int n
   if (idx >= static_cast<long long>(T) * chunks) return;
   const int t = static_cast<int>(idx / chunks), c = static_cast<int>(idx % chunks) * 8;
   const int Sk = T * k;
+  // The shared row and, eight slots at a time, the slot positions, weights and
+  // rows are loaded with clamped indices before any is used, so each group of
+  // loads is in flight together.
+  const uint4 vsh = *reinterpret_cast<const uint4*>(
+      y_slots + static_cast<size_t>(n_shared ? Sk + t : 0) * H + c);
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int pos = slot_pos[static_cast<size_t>(t) * k + j];
-    if (pos < 0 || pos >= Sk) {
-      status_set(status, MOE_STATUS_BAD_INDEX);
-      continue;
-    }
-    const float w = topk_w[static_cast<size_t>(t) * k + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(y_slots + static_cast<size_t>(pos) * H + c);
-    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+  auto group = [&](int j0) {
+    int pos[8];
+    float w[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = __builtin_fmaf(w, bf16_to_f32(p[i] & 0xFFFFu), acc[2 * i]);
-      acc[2 * i + 1] = __builtin_fmaf(w, bf16_to_f32(p[i] >> 16), acc[2 * i + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const size_t sj = static_cast<size_t>(t) * k + min(j0 + u, k - 1);
+      pos[u] = slot_pos[sj];
+      w[u] = topk_w[sj];
     }
-  }
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = (pos[u] >= 0 && pos[u] < Sk) ? pos[u] : 0;
+      v[u] = *reinterpret_cast<const uint4*>(y_slots + static_cast<size_t>(p) * H + c);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u >= k) break;
+      if (pos[u] < 0 || pos[u] >= Sk) {
+        status_set(status, MOE_STATUS_BAD_INDEX);
+        continue;
+      }
+      const uint32_t p[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(w[u], bf16_to_f32(p[i] & 0xFFFFu), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(w[u], bf16_to_f32(p[i] >> 16), acc[2 * i + 1]);
+      }
+    }
+  };
+  group(0);  // peeled: nothing waits for the shared row before it
+  for (int j0 = 8; j0 < k; j0 += 8) group(j0);
   if (n_shared) {
-    const uint4 v = *reinterpret_cast<const uint4*>(y_slots + static_cast<size_t>(Sk + t) * H + c);
-    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t p[4] = {vsh.x, vsh.y, vsh.z, vsh.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += bf16_to_f32(p[i] & 0xFFFFu);

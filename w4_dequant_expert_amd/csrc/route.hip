@@ -36,10 +36,11 @@ namespace moe {
 // inputs at a time.
 // ---------------------------------------------------------------------------
 constexpr int kTW = 8, kEW = 8;  // per-lane tile: 64 outputs
+constexpr int kShortT = 16;      // batches up to this size use the short-batch kernel
 
-template <int WT, int WE, int CH>
+template <int WT, int WE, int CH, bool VEC>
 __global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
-    int T, int H, int E, int vec_wr, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wr,
     const float* __restrict__ bias, float* __restrict__ logits, uint32_t* __restrict__ bits,
     int nbits, uint32_t* __restrict__ status) {
   constexpr int NT = WT * WE * 64;
@@ -72,46 +73,42 @@ __global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
   constexpr int XI = (XN + NT - 1) / NT, WI = (WN + NT - 1) / NT;
   const int nchunk = H / 64;
   uint4 xr[XI];
-  float4 wrg[WI];
+  u32x4 wrg[WI];  // router values as raw bits (native vectors: they stay in registers)
+  // Loads are unconditional, with clamped indices, so that all of a chunk's
+  // loads are in flight together: a clamped token row or chunk only feeds
+  // outputs that are never stored or chunks that are never multiplied.
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       // consecutive lanes take consecutive tokens, so the transposed LDS
       // writes below fall in different banks
-      const int idx = tid + i * NT;
+      const int idx = min(tid + i * NT, XN - 1);
       const int t = idx % RT, part = idx / RT;
       const int c = part / 8, m = (part % 8) * 8;
-      const int gt = t0 + t, hc = c0 + c;
-      xr[i] = make_uint4(0, 0, 0, 0);
-      if (idx < XN && gt < T && hc < nchunk)
-        xr[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(gt) * H + hc * 64 + m);
+      const int gt = min(t0 + t, T - 1), hc = min(c0 + c, nchunk - 1);
+      xr[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(gt) * H + hc * 64 + m);
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
-      const int idx = tid + i * NT;
+      const int idx = min(tid + i * NT, WN - 1);
       const int row = idx / (RE / 4), col = (idx % (RE / 4)) * 4;
       const int c = row / 64, m = row % 64;
-      const int h = (c0 + c) * 64 + m;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (idx < WN && c0 + c < nchunk) {
-        const float* src = wr + static_cast<size_t>(h) * E + e0 + col;
-        if (vec_wr && e0 + col + 3 < E) {
-          v = *reinterpret_cast<const float4*>(src);
-        } else {
-          if (e0 + col + 0 < E) v.x = src[0];
-          if (e0 + col + 1 < E) v.y = src[1];
-          if (e0 + col + 2 < E) v.z = src[2];
-          if (e0 + col + 3 < E) v.w = src[3];
-        }
+      const int h = min(c0 + c, nchunk - 1) * 64 + m;
+      const float* src = wr + static_cast<size_t>(h) * E;
+      if constexpr (VEC) {  // E % 4 == 0 and 16-byte rows: a clamped column stays in the row
+        wrg[i] = *reinterpret_cast<const u32x4*>(src + min(e0 + col, E - 4));
+      } else {
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+        wrg[i] = u32x4{s32[min(e0 + col, E - 1)], s32[min(e0 + col + 1, E - 1)],
+                       s32[min(e0 + col + 2, E - 1)], s32[min(e0 + col + 3, E - 1)]};
       }
-      wrg[i] = v;
     }
   };
   auto store_chunk = [&]() {
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int idx = tid + i * NT;
-      if (idx < XN) {
+      if (XN % NT == 0 || idx < XN) {
         const int t = idx % RT, part = idx / RT;
         const int c = part / 8, m = (part % 8) * 8;
         const uint32_t wv[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
@@ -125,9 +122,9 @@ __global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
       const int idx = tid + i * NT;
-      if (idx < WN) {
+      if (WN % NT == 0 || idx < WN) {
         const int row = idx / (RE / 4), col = (idx % (RE / 4)) * 4;
-        *reinterpret_cast<float4*>(&ws[row / 64][row % 64][col]) = wrg[i];
+        *reinterpret_cast<u32x4*>(&ws[row / 64][row % 64][col]) = wrg[i];
       }
     }
   };
@@ -182,30 +179,116 @@ __global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// K2: top-k and weights.  A token is served by one 16-lane row of a wave
-// (four tokens per wave); lane r holds the scores of experts r, r+16, r+32...
-// Each of the k rounds takes the lane-local best unselected expert and reduces
-// across the row with four DPP exchanges (row mirror, half-row mirror, quad
-// swaps by 2 and by 1, which pair every lane with every other through the
-// butterfly), ordering by higher score and then lower expert index.
+// K1 for short batches (decode): the same scores in the same evaluation order,
+// with the work spread over the router matrix instead of over tokens, so that
+// its 4*H*E bytes stream through many compute units at once.  A workgroup owns
+// 16 experts; thread (m, e) runs the fma chain of partial m of expert e for
+// every token, reading each of its router weights once.  The 64 partials of a
+// (token, expert) then meet in LDS, where one thread applies the tree
+// p[i] += p[i+s], s = 32..1, and adds the bias.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
+constexpr int kShortHC = 1024;           // inputs of x staged per pass
+constexpr int kShortIU = kShortHC / 64;  // chain steps per pass
+
+template <int TT>  // batch bucket: T <= TT; rows T..TT-1 are computed and dropped
+__global__ __launch_bounds__(1024) void router_scores_short_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, float* __restrict__ logits, uint32_t* __restrict__ bits,
+    int nbits, uint32_t* __restrict__ status) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[TT][kShortHC];
+  __shared__ float ps[TT][64][17];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int es = lane & 15, m = (tid >> 6) * 4 + (lane >> 4);
+  const int e = blockIdx.x * 16 + es, ec = min(e, E - 1);
+
+  {  // clear the token bitmask of K2 and the status word
+    for (int i = blockIdx.x * 1024 + tid; i < nbits; i += gridDim.x * 1024) bits[i] = 0u;
+    if (blockIdx.x == 0 && tid == 0 && status) *status = 0u;
+  }
+
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+
+  for (int c = 0; c < H; c += kShortHC) {
+    const int ni = min(kShortHC, H - c) / 64;  // chain steps of this pass
+    float wv[kShortIU];
+#pragma unroll
+    for (int i = 0; i < kShortIU; ++i)
+      wv[i] = wr[static_cast<size_t>(c + min(i, ni - 1) * 64 + m) * E + ec];
+    // x[0..T)[c .. c + 64 ni) as bfloat16, 16 bytes per thread and pass
+    const int nq = T * ni * 8;
+    uint4 xv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = min(tid + u * 1024, nq - 1);
+      const int t = q / (ni * 8), cc = q % (ni * 8);
+      xv[u] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + c + cc * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + u * 1024;
+      if (q < nq) {
+        const int t = q / (ni * 8), cc = q % (ni * 8);
+        *reinterpret_cast<uint4*>(&xs[t][cc * 8]) = xv[u];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kShortIU; ++i) {
+      if (i < ni) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+          acc[t] = __builtin_fmaf(bf16_to_f32(xs[t][i * 64 + m]), wv[i], acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) ps[t][m][es] = acc[t];
+  __syncthreads();
+  if (tid < T * 16) {
+    const int t = tid >> 4, j = tid & 15;
+    const int eo = blockIdx.x * 16 + j;
+    float p[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) p[i] = ps[t][i][j];
+#pragma unroll
+    for (int s2 = 32; s2 >= 1; s2 >>= 1)
+#pragma unroll
+      for (int i = 0; i < s2; ++i) p[i] = p[i] + p[i + s2];
+    if (eo < E) {
+      float l = p[0];
+      if (bias) l = l + bias[eo];
+      logits[static_cast<size_t>(t) * E + eo] = l;
+    }
+  }
 }
 
+// ---------------------------------------------------------------------------
+// K2: top-k and weights.  A token is served by one 16-lane row of a wave
+// (four tokens per wave); lane r holds the scores of experts r, r+16, r+32...
+// Every score becomes a 64-bit key: an order-preserving image of the float32
+// score in the high word and the complemented expert index in the low word,
+// so that a larger key means a higher score or, between equal scores, a lower
+// expert index (the selection order), and no two keys are equal.  Round j
+// takes each lane's largest key below the previous round's winner and the
+// row maximum of those over four DPP exchanges (row mirror, half-row mirror,
+// quad swaps by 2 and by 1, which pair every lane with every other through
+// the butterfly).  The rounds are branch-free.
+// ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& bv, int& be) {
-  const float ov = __int_as_float(dpp<CTRL>(__float_as_int(bv)));
-  const int oe = dpp<CTRL>(be);
-  if (better(ov, oe, bv, be)) {
-    bv = ov;
-    be = oe;
-  }
+__device__ __forceinline__ uint64_t max_step(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp<CTRL>(static_cast<int>(v)));
+  const uint32_t hi = static_cast<uint32_t>(dpp<CTRL>(static_cast<int>(v >> 32)));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
 }
 
 template <int CTRL>
@@ -215,6 +298,16 @@ __device__ __forceinline__ float sum_step(float v) {
 
 constexpr int kRowMirror = 0x140, kHalfMirror = 0x141;
 constexpr int kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;  // quad_perm [2,3,0,1] and [1,0,3,2]
+
+// Order-preserving map of a float32 (not NaN, -0 already folded into +0) to
+// an unsigned integer, and back.
+__device__ __forceinline__ uint32_t float_order(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
 
 template <int VPL>  // scores per lane: E <= 16 * VPL
 __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
@@ -227,75 +320,63 @@ __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
   const int r = lane & 15;
   const int t = blockIdx.x * 16 + (tid >> 4);
   const bool tok_ok = t < T;
-  const int tt = tok_ok ? t : 0;  // rows past T work on token 0 and store nothing
+  const int tt = tok_ok ? t : T - 1;  // rows past T work on a real token and store nothing
 
+  // every load is issued unconditionally (clamped index), all in flight together
   float val[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) val[v] = logits[static_cast<size_t>(tt) * E + min(r + 16 * v, E - 1)];
   bool saw_nan = false;
+  uint64_t key[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = r + 16 * v;
-    float s = -INFINITY;
-    if (e < E) {
-      s = logits[static_cast<size_t>(tt) * E + e];
-      if (s != s) {
-        saw_nan = true;
-        s = -INFINITY;
-      }
-    }
-    val[v] = s;
+    const float sc = val[v];
+    saw_nan |= (e < E) && (sc != sc);
+    const float f = (sc == sc) ? sc + 0.0f : -INFINITY;  // NaN ranks as -inf; -0 as +0
+    const uint64_t kk = (static_cast<uint64_t>(float_order(f)) << 32) | static_cast<uint32_t>(~e);
+    key[v] = (e < E) ? kk : 0ull;  // 0 is below every real key
   }
-  uint64_t taken = 0;
-  float sel_v[2] = {-INFINITY, -INFINITY};  // selections r and r + 16 of this token
-  int sel_e[2] = {0, 0};
+
+  uint64_t prev = ~0ull;
+  uint64_t sel0 = 0, sel1 = 0;  // this lane's selections: ranks r and r + 16
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
+    uint64_t best = 0;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = r + 16 * v;
-      if (e < E && !((taken >> v) & 1ull) && better(val[v], e, bv, be)) {
-        bv = val[v];
-        be = e;
-      }
-    }
-    argmax_step<kRowMirror>(bv, be);
-    argmax_step<kHalfMirror>(bv, be);
-    argmax_step<kQuadSwap2>(bv, be);
-    argmax_step<kQuadSwap1>(bv, be);
-    if ((be & 15) == r) taken |= 1ull << (be >> 4);
-    if (j == r) {
-      sel_v[0] = bv;
-      sel_e[0] = be;
-    }
-    if (j == r + 16) {
-      sel_v[1] = bv;
-      sel_e[1] = be;
-    }
+    for (int v = 0; v < VPL; ++v) best = (key[v] < prev && key[v] > best) ? key[v] : best;
+    best = max_step<kRowMirror>(best);
+    best = max_step<kHalfMirror>(best);
+    best = max_step<kQuadSwap2>(best);
+    best = max_step<kQuadSwap1>(best);
+    prev = best;
+    sel0 = (j == r) ? best : sel0;
+    sel1 = (j == r + 16) ? best : sel1;
   }
+  const float sv0 = order_float(static_cast<uint32_t>(sel0 >> 32));
+  const float sv1 = order_float(static_cast<uint32_t>(sel1 >> 32));
+  const int se0 = static_cast<int>(~static_cast<uint32_t>(sel0));
+  const int se1 = static_cast<int>(~static_cast<uint32_t>(sel1));
+
   // weights: exp(l_j - l_max) / sum over the selected (the softmax
   // denominator over all experts cancels in the renormalisation)
-  const float top = __int_as_float(__shfl(__float_as_int(sel_v[0]), lane & ~15, 64));
-  float ex[2];
-  float den = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int j = r + 16 * q;
-    ex[q] = (j < k) ? __expf(sel_v[q] - top) : 0.0f;
-    den += ex[q];
-  }
+  const float top = __int_as_float(__shfl(__float_as_int(sv0), lane & ~15, 64));
+  const float ex0 = (r < k) ? __expf(sv0 - top) : 0.0f;
+  const float ex1 = (r + 16 < k) ? __expf(sv1 - top) : 0.0f;
+  float den = ex0 + ex1;
   den = sum_step<kRowMirror>(den);
   den = sum_step<kHalfMirror>(den);
   den = sum_step<kQuadSwap2>(den);
   den = sum_step<kQuadSwap1>(den);
   if (tok_ok) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int j = r + 16 * q;
-      if (j < k) {
-        topk_idx[static_cast<size_t>(t) * k + j] = sel_e[q];
-        topk_w[static_cast<size_t>(t) * k + j] = ex[q] / den;
-        atomicOr(&bits[static_cast<size_t>(t >> 5) * E + sel_e[q]], 1u << (t & 31));
-      }
+    if (r < k) {
+      topk_idx[static_cast<size_t>(t) * k + r] = se0;
+      topk_w[static_cast<size_t>(t) * k + r] = ex0 / den;
+      atomicOr(&bits[static_cast<size_t>(t >> 5) * E + se0], 1u << (t & 31));
+    }
+    if (r + 16 < k) {
+      topk_idx[static_cast<size_t>(t) * k + r + 16] = se1;
+      topk_w[static_cast<size_t>(t) * k + r + 16] = ex1 / den;
+      atomicOr(&bits[static_cast<size_t>(t >> 5) * E + se1], 1u << (t & 31));
     }
   }
   if (saw_nan && tok_ok) status_set(status, MOE_STATUS_NAN_LOGIT);
@@ -330,6 +411,8 @@ __device__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total
   return r;
 }
 
+constexpr int kScatterU = 16;  // slots per thread per scatter pass
+
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     int T, int E, int k, int n_shared, int tile_m_max, int tile_gran,
     const uint32_t* __restrict__ bits, int32_t* __restrict__ pref, int32_t* __restrict__ counts,
@@ -352,8 +435,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   const bool scanner = tid < E * tpe;
   const int w0 = scanner ? static_cast<int>(static_cast<long long>(q) * W / tpe) : 0;
   const int w1 = scanner ? static_cast<int>(static_cast<long long>(q + 1) * W / tpe) : 0;
+  // words are read eight at a time with clamped indices, so each batch of
+  // loads is in flight together
   int part = 0;
-  for (int w = w0; w < w1; ++w) part += __popc(bits[static_cast<size_t>(w) * E + e]);
+  for (int w = w0; w < w1; w += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = bits[static_cast<size_t>(min(w + u, w1 - 1)) * E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) part += (w + u < w1) ? __popc(v[u]) : 0;
+  }
   s_part[tid] = part;
   __syncthreads();
   int cnt = 0;
@@ -365,9 +456,17 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
       cnt += v;
     }
     int run = base;
-    for (int w = w0; w < w1; ++w) {
-      pref[static_cast<size_t>(w) * E + e] = run;
-      run += __popc(bits[static_cast<size_t>(w) * E + e]);
+    for (int w = w0; w < w1; w += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = bits[static_cast<size_t>(min(w + u, w1 - 1)) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (w + u < w1) {
+          pref[static_cast<size_t>(w + u) * E + e] = run;
+          run += __popc(v[u]);
+        }
+      }
     }
   }
   int total = 0;
@@ -421,28 +520,24 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     reinterpret_cast<int4*>(blocks)[b] = make_int4(g, first, rows, tm);
   }
 
-  // stable scatter: row = expert offset + tokens before t that chose e; four
-  // slots per thread per pass so their loads overlap
-  for (int s0 = tid; s0 < S; s0 += 4 * 1024) {
-    int ex[4];
+  // stable scatter: row = expert offset + tokens before t that chose e;
+  // kScatterU slots per thread per pass, their loads issued together
+  for (int s0 = tid; s0 < S; s0 += kScatterU * 1024) {
+    int ex[kScatterU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u * 1024;
-      ex[u] = (s < S) ? topk_idx[s] : 0;
-    }
-    uint32_t wbits[4];
-    int wpref[4];
+    for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(s0 + u * 1024, S - 1)];
+    uint32_t wbits[kScatterU];
+    int wpref[kScatterU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u * 1024;
-      const int t = (s < S) ? s / k : 0;
+    for (int u = 0; u < kScatterU; ++u) {
+      const int t = min(s0 + u * 1024, S - 1) / k;
       const int e = min(max(ex[u], 0), E - 1);
       const size_t wi = static_cast<size_t>(t >> 5) * E + e;
       wbits[u] = bits[wi];
       wpref[u] = pref[wi];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kScatterU; ++u) {
       const int s = s0 + u * 1024;
       if (s >= S) continue;
       if (ex[u] < 0 || ex[u] >= E) {
@@ -468,14 +563,33 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
   const int nbits = ((T + 31) / 32) * E;
   // 16-byte router loads only when every row start is 16-byte aligned
   const int vec_wr = (E % 4 == 0) && (reinterpret_cast<uintptr_t>(wr) % 16 == 0);
-  if (T >= 1024) {  // 32 x 32 tiles, 16 waves
+  if (T <= kShortT) {  // decode-sized batches: spread over the router matrix
+    const dim3 g((E + 15) / 16);
+#define MOE_SHORT(TT)                                                                      \
+  hipLaunchKernelGGL(router_scores_short_kernel<TT>, g, dim3(1024), 0, stream, T, d.H, E, x, wr, \
+                     bias, rb.logits, rb.bits, nbits, rb.status)
+    if (T <= 1) MOE_SHORT(1);
+    else if (T <= 2) MOE_SHORT(2);
+    else if (T <= 4) MOE_SHORT(4);
+    else if (T <= 8) MOE_SHORT(8);
+    else MOE_SHORT(16);
+#undef MOE_SHORT
+  } else if (T >= 1024) {  // 32 x 32 tiles, 16 waves
     const dim3 g1((T + 31) / 32, (E + 31) / 32);
-    hipLaunchKernelGGL((router_scores_kernel<4, 4, 2>), g1, dim3(1024), 0, stream, T, d.H, E,
-                       vec_wr, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
+    if (vec_wr)
+      hipLaunchKernelGGL((router_scores_kernel<4, 4, 2, true>), g1, dim3(1024), 0, stream, T,
+                         d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
+    else
+      hipLaunchKernelGGL((router_scores_kernel<4, 4, 2, false>), g1, dim3(1024), 0, stream, T,
+                         d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
   } else {  // 16 x 16 tiles, 4 waves: more workgroups for short batches
     const dim3 g1((T + 15) / 16, (E + 15) / 16);
-    hipLaunchKernelGGL((router_scores_kernel<2, 2, 4>), g1, dim3(256), 0, stream, T, d.H, E,
-                       vec_wr, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
+    if (vec_wr)
+      hipLaunchKernelGGL((router_scores_kernel<2, 2, 4, true>), g1, dim3(256), 0, stream, T,
+                         d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
+    else
+      hipLaunchKernelGGL((router_scores_kernel<2, 2, 4, false>), g1, dim3(256), 0, stream, T,
+                         d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
   }
   const dim3 g2((T + 15) / 16);
   if (E <= 256)
