@@ -63,11 +63,20 @@ struct BlockInfo {
   const uint8_t* P;  // packed matrix of this block's expert
 };
 
+// Workgroups are dealt to the eight XCDs round-robin (workgroup i runs on
+// XCD i mod 8).  Blocks are dealt the same way -- block b to XCD b mod 8 --
+// with all N tiles of a block, which read the same activation rows, on the
+// block's XCD so that they share its L2: workgroup i takes block
+// 8 * ((i / 8) / ntiles) + i mod 8 and N tile (i / 8) mod ntiles.  The grid
+// holds ceil(blocks / 8) * 8 * ntiles workgroups.
+constexpr int kXcds = 8;
+
 template <bool GATE_UP>
 __device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi) {
   const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
-  const int bid = blockIdx.x / ntiles;
-  bi.nt = blockIdx.x % ntiles;
+  const int r = blockIdx.x / kXcds;
+  const int bid = kXcds * (r / ntiles) + blockIdx.x % kXcds;
+  bi.nt = r % ntiles;
   const int nblk = min(*a.n_blocks, a.max_blocks);
   if (bid >= nblk) return false;
   const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
@@ -252,153 +261,279 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
 }
 
 // ---------------------------------------------------------------------------
-// Tall-tile kernel: blocks of 48..128 rows.  Four waves, four slices each,
-// every wave holding all of the block's tile rows of accumulators.  The block
-// body is instantiated per tile height (MT = 3..8 row tiles of 16), so its
-// step loop has no per-row-tile branches, and the weights of step s+1 are
-// rebuilt between the MFMAs of step s (two B buffers): the VALU work of the
-// reconstruction overlaps the matrix units instead of preceding them.
+// Tall-tile kernel: blocks of 48..128 rows, computed as MT = 2..4 row tiles of
+// 32 with v_mfma_f32_32x32x16_bf16 (on gfx950 the 32x32 form delivers twice
+// the 16x16 form's throughput).  Eight waves, two per SIMD: each owns two
+// weight slices (one 32-column tile) and all of the block's rows, so each
+// rebuilt weight feeds MT MFMAs, and the two waves of a SIMD overlap each
+// other's matrix, vector and LDS work (one wave per SIMD leaves the matrix
+// core and LDS about half used).
+//   - Activations and packed codes are copied from memory straight into LDS
+//     (global_load_lds) two steps ahead, through three rotating buffers.
+//     A row's sixteen 16-byte chunks are stored XOR-swizzled by the row
+//     index, so rows need no padding and the MFMA reads are conflict-free.
+//   - The weights of MFMA k-chunk j+1 are rebuilt while the MFMAs of chunk j
+//     run; the codes of a step are read from LDS into registers at the end
+//     of the previous step.
+//   - The step loop has no divergent branches: a wave past the last slice
+//     (partial N tile) computes on a clamped slice and stores nothing; rows
+//     past the block copy a real row whose outputs are dropped; inputs past K
+//     are zeroed in LDS once their copy has landed.
+// MFMA operand convention (32x32x16): lane l supplies row l mod 32 of A and
+// column l mod 32 of B with eight consecutive reduction elements; in k-chunk
+// j of a step (j = 0..7) lane l carries inputs 16j + 8*(l/32) .. +7.  Lane l
+// receives D column l mod 32, rows 8*(i/4) + 4*(l/32) + (i mod 4), i = 0..15.
 // ---------------------------------------------------------------------------
 constexpr int kTallM = 128;
+constexpr int kTallWaves = 8;
+constexpr int kTallThreads = kTallWaves * kWave;
+constexpr int kTallBuf = kTallM * kKS * 2;      // bytes of one staged activation step
+constexpr int kCodeSlot = 1280;                 // LDS bytes per (slice, step): 1024 codes + 256
+constexpr int kCodeBuf = kTallWaves * 2 * kCodeSlot;  // one step's codes, two slices a wave
+
+// Workgroup barrier for LDS data whose copies the caller has already waited
+// for.  A plain __syncthreads() would also wait for every copy into LDS still
+// in flight (the prefetch of later steps); the asm's memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One step's codes of a 32-column tile for one lane: eight code words (k-chunk
+// j in q[j]) and the scale/bias words of the step's two input groups.
+struct TileCodes {
+  uint32_t q[8];
+  uint32_t sb[2];
+};
 
 template <int MT, bool GATE_UP>
 __device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& bi,
                                            const uint16_t* __restrict__ src,
-                                           uint16_t* __restrict__ out,
-                                           uint16_t (*As)[kTallM * kLDA], const int* s_tok) {
+                                           uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
+                                           uint8_t* As2, uint8_t* Cs0, uint8_t* Cs1, uint8_t* Cs2,
+                                           const int* s_tok) {
+  constexpr int NCP = MT;  // activation copies per wave per step (4 rows each)
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int nk = pack_steps(K);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int n = lane & 15;
-  const int lk = (lane >> 4) * 32;
   const int row0 = bi.row0, rows = bi.rows;
 
-  const int c_first = bi.nt * 16 + wave * 4;
-  const bool active = c_first < nslices;  // a wave's four slices are all on or all off
-  const uint8_t* sbase = bi.P + static_cast<size_t>(active ? c_first : 0) * nk * kPackBlock;
+  // nslices is even, so a wave's two slices are both in or both out
+  const int c_first = bi.nt * 16 + wave * 2;
+  const bool active = c_first < nslices;
+  const int c0 = min(c_first, nslices - 2);
+  const uint8_t* sbase = bi.P + static_cast<size_t>(c0) * nk * kPackBlock;
   const size_t sstride = static_cast<size_t>(nk) * kPackBlock;
 
-  // A staging: chunk i of this thread is tile row (tid + 256 i) / 16 and
-  // 16-byte column tid % 16; rows past the block read row 0 and are zeroed.
-  const int ac = tid & 15;
-  int arow[MT];  // source row (token for gate/up, h row for down); -1 = pad
+  // Activation copies: copy i of wave w moves tile rows 4q .. 4q+3, q = 8i + w,
+  // into LDS bytes [1024 q, 1024 q + 1024); lane -> row 4q + lane/16, stored
+  // chunk lane % 16, which holds the row's chunk cg = (lane % 16) ^ (row % 16).
+  const int cg = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
+  const uint16_t* arow[NCP];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int m = (tid + 256 * i) >> 4;
-    int r = -1;
-    if (m < rows) r = GATE_UP ? s_tok[m] : row0 + m;
-    arow[i] = r;
+  for (int i = 0; i < NCP; ++i) {
+    const int r = min(4 * (kTallWaves * i + wave) + (lane >> 4), rows - 1);
+    const int srow = GATE_UP ? max(s_tok[r], 0) : row0 + r;
+    arow[i] = src + static_cast<size_t>(srow) * K;
   }
-  auto load_a = [&](int s, uint4 (&ar)[MT]) {
-    const int kk = min(s * kKS + ac * 8, K - 8);
+  auto issue_a = [&](int s, uint8_t* buf) {
+    const int kk = min(min(s, nk - 1) * kKS + cg * 8, K - 8);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-      ar[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(max(arow[i], 0)) * K + kk);
+    for (int i = 0; i < NCP; ++i)
+      __builtin_amdgcn_global_load_lds(arow[i] + kk, buf + (kTallWaves * i + wave) * 1024, 16, 0, 0);
   };
-  auto store_a = [&](int buf, uint4 (&ar)[MT], int s) {
-    const bool kin = s < nk && s * kKS + ac * 8 < K;
+  const bool ktail = (K % kKS) != 0;
+  // after step s's copy has landed: zero the chunks past K (last step only)
+  auto zero_tail = [&](int s, uint8_t* buf) {
+    if (ktail && s == nk - 1 && s * kKS + cg * 8 >= K) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int m = (tid + 256 * i) >> 4;
-      const uint4 v = (arow[i] >= 0 && kin) ? ar[i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&As[buf][m * kLDA + ac * 8]) = v;
+      for (int i = 0; i < NCP; ++i)
+        *reinterpret_cast<uint4*>(buf + (kTallWaves * i + wave) * 1024 + lane * 16) =
+            make_uint4(0, 0, 0, 0);
     }
   };
-  auto load_codes = [&](int s, SliceOps (&o)[4]) {
+  // Code copies of one step for this wave's two slices (four copies): each
+  // slice's 1024 code bytes (16 a lane), then its 128 scale/bias bytes (4 a
+  // lane, the upper half of the wave repeating the lower half so nothing is
+  // read past the block) into this wave's slots of a code buffer.
+  const int cw = wave * (2 * kCodeSlot);
+  auto issue_codes = [&](int s, uint8_t* cbuf) {
     const size_t off = static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) load_slice(sbase + ns * sstride + off, lane, o[ns]);
+    for (int ns = 0; ns < 2; ++ns) {
+      const uint8_t* blk = sbase + ns * sstride + off;
+      __builtin_amdgcn_global_load_lds(blk + lane * 16, cbuf + cw + ns * kCodeSlot, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(blk + kPackScales + (lane & 31) * 4,
+                                       cbuf + cw + ns * kCodeSlot + 1024, 4, 0, 0);
+    }
   };
-  // rebuild word w (0..15: slice w/4, 32-bit word w%4) of a code slot
-  auto rebuild_word = [&](const SliceOps (&o)[4], bf16x8 (&b)[4][4], int w) {
-    const SliceOps& so = o[w >> 2];
-    const float sc = bf16_to_f32(so.sb & 0xFFFFu), bi2 = bf16_to_f32(so.sb >> 16);
-    const uint32_t q = (w & 3) == 0 ? so.q.x : (w & 3) == 1 ? so.q.y : (w & 3) == 2 ? so.q.z : so.q.w;
-    b[w >> 2][w & 3] = as_bf16x8(dequant8(q, sc, bi2));
+  // Lane l reads column n = l mod 32 of the tile, i.e. row n mod 16 of slice
+  // n/16.  In the packed block, the inputs 32p .. 32p+31 of that row are the
+  // 16 bytes at (16p + row) * 16; k-chunk j (inputs 16j + 8h .., h = l/32) is
+  // word 2 (j mod 2) + h of chunk p = j/2.  The codes of a step are read in
+  // one asm block that ends with its own lgkmcnt wait: the compiler cannot
+  // tell which of the copies in flight such reads depend on and would
+  // otherwise wait for all of them; the explicit vmcnt waits before each call
+  // cover the copies they need.
+  const int h = lane >> 5, nrow = lane & 15, nsl = (lane >> 4) & 1;
+  auto read_codes = [&](const uint8_t* cbuf, TileCodes& tc) {
+    const uint8_t* slot = cbuf + cw + nsl * kCodeSlot;
+    const uint32_t ac = lds_addr(slot + nrow * 16);
+    const uint32_t as = lds_addr(slot + kPackScales + (nrow >> 2) * 16);
+    u32x4 c[4], g[2];
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:256\n\t"
+        "ds_read_b128 %2, %6 offset:512\n\t"
+        "ds_read_b128 %3, %6 offset:768\n\t"
+        "ds_read_b128 %4, %7\n\t"
+        "ds_read_b128 %5, %7 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(g[0]), "=&v"(g[1])
+        : "v"(ac), "v"(as));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      tc.q[2 * p] = h ? c[p].y : c[p].x;
+      tc.q[2 * p + 1] = h ? c[p].w : c[p].z;
+    }
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const uint32_t lo = (nrow & 1) ? g[gg].y : g[gg].x, hi = (nrow & 1) ? g[gg].w : g[gg].z;
+      tc.sb[gg] = (nrow & 2) ? hi : lo;
+    }
   };
+  // weights of k-chunk j of the tile
+  auto rebuild_j = [&](const TileCodes& tc, int j) -> bf16x8 {
+    const uint32_t sbw = tc.sb[j >> 2];
+    return as_bf16x8(dequant8(tc.q[j], bf16_to_f32(sbw & 0xFFFFu), bf16_to_f32(sbw >> 16)));
+  };
+  // LDS byte offset of this lane's A fragment for k-chunk j within a 32-row tile
+  const int arow_l = lane & 31;
+  int aoff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) aoff[j] = arow_l * (kKS * 2) + (((2 * j + h) ^ (arow_l & 15)) * 16);
 
-  f32x4 acc[MT][4];
+  f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
 
-  constexpr int WPER = (16 + MT - 1) / MT;  // rebuilt words per row tile
-  // One step: MFMAs of step s on bcur; in between, rebuild step s+1 (slot
-  // cnext) into bnext; then refill cnext with the codes of step s+3.
-  auto step = [&](int s, bf16x8 (&bcur)[4][4], bf16x8 (&bnext)[4][4], SliceOps (&cnext)[4],
-                  int buf, uint4 (&ar)[MT]) {
-    if (active) {
+  // Every global load of the step loop is a copy into LDS; step s issues the
+  // activations of step s+2 (MT copies), then the codes of step s+2 (four
+  // copies), into the third of three rotating buffers.  So "all but the last
+  // MT + 4 copies done" at the start of step s means the activations and
+  // codes of step s have landed, and before the last k-chunk of step s it
+  // means the codes of step s+1 have.  The scheduling barriers keep the
+  // copies in program order around those waits.  The buffers are separate
+  // LDS arrays selected at compile time (the loop body is three steps), so
+  // the compiler sees which copies an activation read depends on; the codes
+  // of step s are read into registers at the end of step s-1.
+  constexpr int kInFlight = MT + 4;
+  bf16x8 bq[2];  // rebuilt weights of two k-chunks
+  TileCodes tc;  // codes of the current step
+  auto step = [&](int s, uint8_t* acur, uint8_t* anew, uint8_t* cnext, uint8_t* cnew) {
+    wait_vmcnt<kInFlight>();
+    zero_tail(s, acur);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(s + 2, anew);
+    issue_codes(s + 2, cnew);
+    __builtin_amdgcn_sched_barrier(0);
+    // A fragments are read one k-chunk ahead; each chunk's work is fenced off
+    // from the next, which bounds the live registers.
+    bf16x8 af[2][MT];
+    auto read_a = [&](int j, bf16x8 (&f)[MT]) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk];
-        bf16x8 af[4];
+      for (int mt = 0; mt < MT; ++mt)
+        f[mt] = *reinterpret_cast<const bf16x8*>(acur + mt * 32 * (kKS * 2) + aoff[j]);
+    };
+    read_a(0, af[0]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
+    for (int j = 0; j < 8; ++j) {
+      if (j < 7) read_a(j + 1, af[(j + 1) & 1]);
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bcur[ns][j], acc[mt][ns], 0, 0, 0);
-#pragma unroll
-        for (int w = mt * WPER; w < (mt + 1) * WPER && w < 16; ++w) rebuild_word(cnext, bnext, w);
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bq[j & 1], acc[mt], 0, 0, 0);
+      if (j < 7) {
+        bq[(j + 1) & 1] = rebuild_j(tc, j + 1);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kInFlight>();
+        __builtin_amdgcn_sched_barrier(0);
+        read_codes(cnext, tc);
+        bq[0] = rebuild_j(tc, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    load_codes(s + 3, cnext);
-    store_a(buf ^ 1, ar, s + 1);
-    load_a(s + 2, ar);
-    __syncthreads();
   };
 
-  SliceOps c0[4], c1[4];
-  bf16x8 b0[4][4], b1[4][4];
-  load_codes(0, c0);
-  load_codes(1, c1);
-  uint4 ar[MT];
-  load_a(0, ar);
-  store_a(0, ar, 0);
-  load_a(1, ar);
-#pragma unroll
-  for (int w = 0; w < 16; ++w) rebuild_word(c0, b0, w);
-  load_codes(2, c0);
-  __syncthreads();
-  for (int s = 0; s < nk; s += 2) {
-    step(s, b0, b1, c1, 0, ar);
-    if (s + 1 < nk) step(s + 1, b1, b0, c0, 1, ar);
+  issue_a(0, As0);
+  issue_codes(0, Cs0);
+  issue_a(1, As1);
+  issue_codes(1, Cs1);
+  wait_vmcnt<kInFlight>();  // activations and codes of step 0
+  read_codes(Cs0, tc);
+  bq[0] = rebuild_j(tc, 0);
+  int s = 0;
+  for (; s + 2 < nk; s += 3) {
+    step(s, As0, As2, Cs1, Cs2);
+    step(s + 1, As1, As0, Cs2, Cs0);
+    step(s + 2, As2, As1, Cs0, Cs1);
   }
+  if (s < nk) step(s, As0, As2, Cs1, Cs2);
+  if (s + 1 < nk) step(s + 1, As1, As0, Cs2, Cs0);
   if (!active) return;
 
+  const int n16 = lane & 15;
+  const int c = c_first + nsl;  // slice of this lane's column
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + (lane >> 4) * 4 + i;
+    for (int i = 0; i < 16; ++i) {
+      const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
       const size_t r = static_cast<size_t>(row0 + m);
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        const int c = c_first + ns;
-        const float v = acc[mt][ns][i];
-        if (GATE_UP) {
-          const float u = __shfl_xor(v, 8, 64);
-          if (n < 8 && m < rows) {
-            const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
-            out[r * a.I + c * 8 + n] = f32_to_bf16(hv);
-          }
-        } else if (m < rows) {
-          out[r * a.H + c * 16 + n] = f32_to_bf16(v);
+      const float v = acc[mt][i];
+      if (GATE_UP) {
+        const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
+        if (n16 < 8 && m < rows) {
+          const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+          out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
         }
+      } else if (m < rows) {
+        out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
       }
     }
   }
 }
 
 template <bool GATE_UP>
-__global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
-                                                           const uint16_t* __restrict__ src,
-                                                           uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTallM * kLDA];
+__global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
+                                                                    const uint16_t* __restrict__ src,
+                                                                    uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Cs0[kCodeBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Cs1[kCodeBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Cs2[kCodeBuf];
   __shared__ int s_tok[kTallM];
 
   BlockInfo bi;
@@ -409,13 +544,10 @@ __global__ __launch_bounds__(256) void w4_gemm_tall_kernel(GemmArgs a,
     block_tokens(a, bi, s_tok);
     __syncthreads();
   }
-  switch (bi.tm >> 4) {
-    case 3: tall_block<3, GATE_UP>(a, bi, src, out, As, s_tok); break;
-    case 4: tall_block<4, GATE_UP>(a, bi, src, out, As, s_tok); break;
-    case 5: tall_block<5, GATE_UP>(a, bi, src, out, As, s_tok); break;
-    case 6: tall_block<6, GATE_UP>(a, bi, src, out, As, s_tok); break;
-    case 7: tall_block<7, GATE_UP>(a, bi, src, out, As, s_tok); break;
-    default: tall_block<8, GATE_UP>(a, bi, src, out, As, s_tok); break;
+  switch ((bi.tm + 31) >> 5) {
+    case 2: tall_block<2, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
+    case 3: tall_block<3, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
+    default: tall_block<4, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
   }
 }
 
@@ -582,10 +714,11 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
                               hipStream_t stream) {
   if (a.T <= kGemvRows) return launch_gemv<GATE_UP>(a, src, out, stream);
   const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
-  const dim3 grid(static_cast<unsigned>(a.max_blocks) * ntiles);
+  const long long blocks8 = (a.max_blocks + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid(static_cast<unsigned>(blocks8 * ntiles));
   hipLaunchKernelGGL((w4_gemm_small_kernel<GATE_UP>), grid, dim3(512), 0, stream, a, src, out);
   if (m_max)
-    hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
+    hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, a, src, out);
   return hipGetLastError();
 }
 
