@@ -309,16 +309,16 @@ __device__ __forceinline__ float order_float(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
+// Top-k of token t for one 16-lane row (lane r = lane mod 16): writes the
+// token's indices and weights (t < T) and returns the experts this lane
+// selected (ranks r and r + 16; -1 where the rank is >= k).
 template <int VPL>  // scores per lane: E <= 16 * VPL
-__global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
-                                                          const float* __restrict__ logits,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w,
-                                                          uint32_t* __restrict__ bits,
-                                                          uint32_t* __restrict__ status) {
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ void topk_row(int T, int E, int k, const float* __restrict__ logits,
+                                         int t, int32_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_w, uint32_t* __restrict__ status,
+                                         int& sel_a, int& sel_b) {
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15;
-  const int t = blockIdx.x * 16 + (tid >> 4);
   const bool tok_ok = t < T;
   const int tt = tok_ok ? t : T - 1;  // rows past T work on a real token and store nothing
 
@@ -367,19 +367,33 @@ __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
   den = sum_step<kHalfMirror>(den);
   den = sum_step<kQuadSwap2>(den);
   den = sum_step<kQuadSwap1>(den);
+  sel_a = (tok_ok && r < k) ? se0 : -1;
+  sel_b = (tok_ok && r + 16 < k) ? se1 : -1;
   if (tok_ok) {
     if (r < k) {
       topk_idx[static_cast<size_t>(t) * k + r] = se0;
       topk_w[static_cast<size_t>(t) * k + r] = ex0 / den;
-      atomicOr(&bits[static_cast<size_t>(t >> 5) * E + se0], 1u << (t & 31));
     }
     if (r + 16 < k) {
       topk_idx[static_cast<size_t>(t) * k + r + 16] = se1;
       topk_w[static_cast<size_t>(t) * k + r + 16] = ex1 / den;
-      atomicOr(&bits[static_cast<size_t>(t >> 5) * E + se1], 1u << (t & 31));
     }
   }
   if (saw_nan && tok_ok) status_set(status, MOE_STATUS_NAN_LOGIT);
+}
+
+template <int VPL>  // scores per lane: E <= 16 * VPL
+__global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
+                                                          const float* __restrict__ logits,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w,
+                                                          uint32_t* __restrict__ bits,
+                                                          uint32_t* __restrict__ status) {
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  int sa, sb;
+  topk_row<VPL>(T, E, k, logits, t, topk_idx, topk_w, status, sa, sb);
+  if (sa >= 0) atomicOr(&bits[static_cast<size_t>(t >> 5) * E + sa], 1u << (t & 31));
+  if (sb >= 0) atomicOr(&bits[static_cast<size_t>(t >> 5) * E + sb], 1u << (t & 31));
 }
 
 // ---------------------------------------------------------------------------
@@ -409,6 +423,69 @@ __device__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total
   *total = tmp[16];
   __syncthreads();
   return r;
+}
+
+// Histogram -> offsets (exclusive scan) and the tile block map, for a
+// workgroup of 1024 threads; thread e < E holds the count of expert e.
+// Leaves the counts and offsets in s_cnt / s_off (index E: the shared group).
+__device__ void finish_tables(int T, int E, int k, int n_shared, int tile_m_max, int tile_gran,
+                              int cnt, int* s_cnt, int* s_off, int* s_bstart, int* tmp,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                              int32_t* __restrict__ blocks, int32_t* __restrict__ n_blocks,
+                              int max_blocks, uint32_t* __restrict__ status) {
+  const int tid = threadIdx.x;
+  const int S = T * k;
+  int total = 0;
+  const int off = block_exclusive_scan((tid < E) ? cnt : 0, tmp, &total);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    s_off[tid] = off;
+    s_cnt[tid] = cnt;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    s_off[E] = S;
+    s_cnt[E] = n_shared ? T : 0;
+    if (total != S) status_set(status, MOE_STATUS_BAD_INDEX);
+  }
+  __syncthreads();
+
+  // block map: blocks per group, scanned into each group's first block
+  const int groups = E + (n_shared ? 1 : 0);
+  int nb = 0;
+  if (tid < groups) {
+    const int c = s_cnt[tid];
+    nb = (c + tile_m_max - 1) / tile_m_max;
+  }
+  int nb_total = 0;
+  const int bstart = block_exclusive_scan(nb, tmp, &nb_total);
+  if (tid < groups) s_bstart[tid] = bstart;
+  if (tid == 0) {
+    s_bstart[groups] = nb_total;
+    if (nb_total > max_blocks) status_set(status, MOE_STATUS_BLOCK_OVERFLOW);
+    *n_blocks = min(nb_total, max_blocks);
+  }
+  __syncthreads();
+  const int nwrite = min(nb_total, max_blocks);
+  for (int b = tid; b < nwrite; b += 1024) {
+    int lo = 0, hi = groups - 1;  // last group whose first block is <= b
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_bstart[mid] <= b) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int c = s_cnt[g];
+    const int ng = s_bstart[g + 1] - s_bstart[g];
+    const int i = b - s_bstart[g];
+    const int bs = c / ng, rem = c % ng;
+    const int rows = bs + (i < rem ? 1 : 0);
+    const int first = (g < E ? s_off[g] : S) + i * bs + min(i, rem);
+    const int tallest = bs + (rem > 0 ? 1 : 0);
+    const int tm = (tallest + tile_gran - 1) / tile_gran * tile_gran;
+    reinterpret_cast<int4*>(blocks)[b] = make_int4(g, first, rows, tm);
+  }
+
 }
 
 constexpr int kScatterU = 16;  // slots per thread per scatter pass
@@ -469,56 +546,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
       }
     }
   }
-  int total = 0;
-  const int off = block_exclusive_scan((tid < E) ? cnt : 0, tmp, &total);
-  if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
-    s_off[tid] = off;
-    s_cnt[tid] = cnt;
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    s_off[E] = S;
-    s_cnt[E] = n_shared ? T : 0;
-    if (total != S) status_set(status, MOE_STATUS_BAD_INDEX);
-  }
-  __syncthreads();
-
-  // block map: blocks per group, scanned into each group's first block
-  const int groups = E + (n_shared ? 1 : 0);
-  int nb = 0;
-  if (tid < groups) {
-    const int c = s_cnt[tid];
-    nb = (c + tile_m_max - 1) / tile_m_max;
-  }
-  int nb_total = 0;
-  const int bstart = block_exclusive_scan(nb, tmp, &nb_total);
-  if (tid < groups) s_bstart[tid] = bstart;
-  if (tid == 0) {
-    s_bstart[groups] = nb_total;
-    if (nb_total > max_blocks) status_set(status, MOE_STATUS_BLOCK_OVERFLOW);
-    *n_blocks = min(nb_total, max_blocks);
-  }
-  __syncthreads();
-  const int nwrite = min(nb_total, max_blocks);
-  for (int b = tid; b < nwrite; b += 1024) {
-    int lo = 0, hi = groups - 1;  // last group whose first block is <= b
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_bstart[mid] <= b) lo = mid; else hi = mid - 1;
-    }
-    const int g = lo;
-    const int c = s_cnt[g];
-    const int ng = s_bstart[g + 1] - s_bstart[g];
-    const int i = b - s_bstart[g];
-    const int bs = c / ng, rem = c % ng;
-    const int rows = bs + (i < rem ? 1 : 0);
-    const int first = (g < E ? s_off[g] : S) + i * bs + min(i, rem);
-    const int tallest = bs + (rem > 0 ? 1 : 0);
-    const int tm = (tallest + tile_gran - 1) / tile_gran * tile_gran;
-    reinterpret_cast<int4*>(blocks)[b] = make_int4(g, first, rows, tm);
-  }
+  finish_tables(T, E, k, n_shared, tile_m_max, tile_gran, cnt, s_cnt, s_off, s_bstart, tmp, counts,
+                offsets, blocks, n_blocks, max_blocks, status);
 
   // stable scatter: row = expert offset + tokens before t that chose e;
   // kScatterU slots per thread per pass, their loads issued together
@@ -557,6 +586,151 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// K3 when the token bitmask fits in LDS (ceil(T/32) * E <= kScanLdsWords):
+// the bitmask is read once, coalesced; the per-expert prefixes, the scan, the
+// block map and the scatter ranks all come from LDS, and the slot experts for
+// the scatter are loaded at the start, so the kernel makes two rounds of
+// global loads instead of four.
+// ---------------------------------------------------------------------------
+constexpr int kScanLdsWords = 16384;
+constexpr int kScanLoads = kScanLdsWords / 1024;
+
+__global__ __launch_bounds__(1024) void route_scan_lds_kernel(
+    int T, int E, int k, int n_shared, int tile_m_max, int tile_gran,
+    const uint32_t* __restrict__ bits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, const int32_t* __restrict__ topk_idx,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos, int32_t* __restrict__ blocks,
+    int32_t* __restrict__ n_blocks, int max_blocks, uint32_t* __restrict__ status) {
+  __shared__ uint32_t s_bits[kScanLdsWords];  // [word][expert]
+  __shared__ int s_pref[kScanLdsWords];       // tokens before each word, per expert
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_bstart[kMaxE + 2];
+  __shared__ int s_cnt[kMaxE + 1];
+  __shared__ int s_part[1024];
+  __shared__ int tmp[17];
+  const int tid = threadIdx.x;
+  const int S = T * k;
+  const int W = (T + 31) / 32;
+  const int nw = W * E;
+
+  // the first scatter round's slot experts, then the whole bitmask
+  int ex[kScatterU];
+#pragma unroll
+  for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(tid + u * 1024, S - 1)];
+  uint32_t bv[kScanLoads];
+#pragma unroll
+  for (int u = 0; u < kScanLoads; ++u) bv[u] = bits[min(tid + u * 1024, nw - 1)];
+#pragma unroll
+  for (int u = 0; u < kScanLoads; ++u)
+    if (tid + u * 1024 < nw) s_bits[tid + u * 1024] = bv[u];
+  __syncthreads();
+
+  // per-expert prefix popcounts: thread (e, q) of the tpe threads of expert e
+  // covers words [q*W/tpe, (q+1)*W/tpe)
+  const int tpe = max(1, 1024 / E);
+  const int e = tid % E, q = tid / E;
+  const bool scanner = tid < E * tpe;
+  const int w0 = scanner ? q * W / tpe : 0;
+  const int w1 = scanner ? (q + 1) * W / tpe : 0;
+  int part = 0;
+  for (int w = w0; w < w1; ++w) part += __popc(s_bits[w * E + e]);
+  s_part[tid] = part;
+  __syncthreads();
+  int cnt = 0;
+  if (scanner) {
+    int base = 0;
+    for (int p = 0; p < tpe; ++p) {
+      const int v = s_part[p * E + e];
+      if (p < q) base += v;
+      cnt += v;
+    }
+    int run = base;
+    for (int w = w0; w < w1; ++w) {
+      s_pref[w * E + e] = run;
+      run += __popc(s_bits[w * E + e]);
+    }
+  }
+  finish_tables(T, E, k, n_shared, tile_m_max, tile_gran, cnt, s_cnt, s_off, s_bstart, tmp, counts,
+                offsets, blocks, n_blocks, max_blocks, status);
+  __syncthreads();  // s_pref complete
+
+  // stable scatter: row = expert offset + tokens before t that chose e
+  for (int s0 = tid; s0 < S; s0 += kScatterU * 1024) {
+    if (s0 != tid) {
+#pragma unroll
+      for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(s0 + u * 1024, S - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterU; ++u) {
+      const int sl = s0 + u * 1024;
+      if (sl >= S) continue;
+      if (ex[u] < 0 || ex[u] >= E) {
+        status_set(status, MOE_STATUS_BAD_INDEX);
+        continue;
+      }
+      const int t = sl / k;
+      const int wi = (t >> 5) * E + ex[u];
+      const int pos = s_off[ex[u]] + s_pref[wi] + __popc(s_bits[wi] & ((1u << (t & 31)) - 1u));
+      if (pos < 0 || pos >= S) {
+        status_set(status, MOE_STATUS_BAD_INDEX);
+        continue;
+      }
+      sorted_slot[pos] = sl;
+      slot_pos[sl] = pos;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2+K3 for short batches (T <= 16): one workgroup does the top-k of every
+// token (16 lanes a token), the histogram and ranks from a per-expert token
+// bitmask kept in LDS, the scan, the block map and the scatter, with no
+// global round trip in between.
+// ---------------------------------------------------------------------------
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_short_kernel(
+    int T, int E, int k, int n_shared, int tile_m_max, int tile_gran,
+    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ blocks, int32_t* __restrict__ n_blocks,
+    int max_blocks, uint32_t* __restrict__ status) {
+  __shared__ uint32_t s_bits[kMaxE];         // bit t: token t selected expert e
+  __shared__ int s_sel[kShortT * kMaxK];     // expert of slot t*k + j
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_bstart[kMaxE + 2];
+  __shared__ int s_cnt[kMaxE + 1];
+  __shared__ int tmp[17];
+  const int tid = threadIdx.x;
+  const int S = T * k;
+  for (int e = tid; e < E; e += 1024) s_bits[e] = 0u;
+  __syncthreads();
+  if (tid < kShortT * 16) {  // a full row of lanes per token slot, t < T or not
+    const int t = tid >> 4, r = tid & 15;
+    int sa, sb;
+    topk_row<VPL>(T, E, k, logits, t, topk_idx, topk_w, status, sa, sb);
+    if (sa >= 0) {
+      s_sel[t * k + r] = sa;
+      atomicOr(&s_bits[sa], 1u << t);
+    }
+    if (sb >= 0) {
+      s_sel[t * k + r + 16] = sb;
+      atomicOr(&s_bits[sb], 1u << t);
+    }
+  }
+  __syncthreads();
+  const int cnt = (tid < E) ? __popc(s_bits[tid]) : 0;
+  finish_tables(T, E, k, n_shared, tile_m_max, tile_gran, cnt, s_cnt, s_off, s_bstart, tmp, counts,
+                offsets, blocks, n_blocks, max_blocks, status);
+  // stable scatter: row = expert offset + tokens before t that chose e
+  for (int sl = tid; sl < S; sl += 1024) {
+    const int t = sl / k, e = s_sel[sl];
+    const int pos = s_off[e] + __popc(s_bits[e] & ((1u << t) - 1u));
+    sorted_slot[pos] = sl;
+    slot_pos[sl] = pos;
+  }
+}
+
+// ---------------------------------------------------------------------------
 hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, const float* bias,
                         const RouteBuffers& rb, hipStream_t stream) {
   const int T = d.T, E = d.E, k = d.k;
@@ -591,6 +765,13 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
       hipLaunchKernelGGL((router_scores_kernel<2, 2, 4, false>), g1, dim3(256), 0, stream, T,
                          d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
   }
+  if (T <= kShortT && E <= 256) {  // top-k, tables and scatter in one workgroup
+    hipLaunchKernelGGL((route_short_kernel<16>), dim3(1), dim3(1024), 0, stream, T, E, k,
+                       d.n_shared, d.tile_m_max, d.tile_gran, rb.logits, rb.topk_idx, rb.topk_w,
+                       rb.counts, rb.offsets, rb.sorted_slot, rb.slot_pos, rb.blocks, rb.n_blocks,
+                       rb.max_blocks, rb.status);
+    return hipGetLastError();
+  }
   const dim3 g2((T + 15) / 16);
   if (E <= 256)
     hipLaunchKernelGGL((router_topk_kernel<16>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
@@ -598,6 +779,13 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
   else
     hipLaunchKernelGGL((router_topk_kernel<64>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
                        rb.topk_idx, rb.topk_w, rb.bits, rb.status);
+  if (static_cast<long long>((T + 31) / 32) * E <= kScanLdsWords) {
+    hipLaunchKernelGGL(route_scan_lds_kernel, dim3(1), dim3(1024), 0, stream, T, E, k, d.n_shared,
+                       d.tile_m_max, d.tile_gran, rb.bits, rb.counts, rb.offsets, rb.topk_idx,
+                       rb.sorted_slot, rb.slot_pos, rb.blocks, rb.n_blocks, rb.max_blocks,
+                       rb.status);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, T, E, k, d.n_shared,
                      d.tile_m_max, d.tile_gran, rb.bits, rb.pref, rb.counts, rb.offsets,
                      rb.topk_idx, rb.sorted_slot, rb.slot_pos, rb.blocks, rb.n_blocks,
