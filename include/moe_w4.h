@@ -88,8 +88,9 @@ typedef struct moe_dims {
  * The GEMMs read the same bytes permuted into a streaming layout, written
  * once by moe_w4_pack: for every 16-row slice and every 128-input step, one
  * 1152-byte block holding the slice's codes in the order the GPU lanes load
- * them followed by the (scale, bias) pairs, with inputs past K padded as code
- * 0, scale 0, bias 0; gate/up slices pair 8 gate rows with their 8 up rows.
+ * them (eight inputs per 32-bit word, nibbles regrouped in pairs) followed by
+ * the (scale, bias) pairs, with inputs past K padded as code 0, scale 0, bias
+ * 0; gate/up slices pair 8 gate rows with their 8 up rows.
  * The packed matrix has moe_w4_packed_bytes(N, K) bytes (4.5 bits per weight
  * when K is a multiple of 128).
  *

@@ -158,14 +158,20 @@ def unpack_host(packed, N, K, gate_up):
         for st in range(nk):
             blk = blocks[c, st]
             codes = blk[:1024].reshape(64, 16)
-            sb = blk[1024:].view(np.uint32).reshape(2, 16)
+            sb = blk[1024:].view(np.uint32).reshape(16, 2).T
+            words = codes.view("<u4").reshape(64, 4)
             for lane in range(64):
                 r, g = lane % 16, lane // 16
-                k0 = st * 128 + g * 32
-                if k0 < K:
-                    q[rows[r], k0 // 2:k0 // 2 + 16] = codes[lane]
-                else:
-                    assert not codes[lane].any()
+                for j in range(4):
+                    k0 = st * 128 + 32 * j + 8 * g
+                    w = int(words[lane, j])
+                    if k0 >= K:
+                        assert w == 0
+                        continue
+                    # pair order: nibble t holds element 2t, nibble t+4 element 2t+1
+                    elems = [(w >> (4 * (e // 2 if e % 2 == 0 else 4 + e // 2))) & 0xF for e in range(8)]
+                    for e in range(0, 8, 2):
+                        q[rows[r], (k0 + e) // 2] = elems[e] | (elems[e + 1] << 4)
             for gg in range(2):
                 grp = st * 2 + gg
                 for r in range(16):

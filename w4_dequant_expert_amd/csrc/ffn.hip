@@ -12,10 +12,10 @@
 //     contiguous h rows for down) are staged in LDS, 128 inputs at a time,
 //     double-buffered, and shared by all waves of the workgroup;
 //   - each wave owns whole 16-row weight slices; a lane loads 16 bytes of
-//     packed codes (32 inputs of one weight row) plus its group's scale and
-//     bias and rebuilds them in registers as the B operand of four
-//     v_mfma_f32_16x16x32_bf16, so each reconstructed weight is used straight
-//     from registers and never stored;
+//     packed codes (four runs of 8 inputs of one weight row) plus the scale
+//     and bias of the step's two groups and rebuilds them in registers as the
+//     B operands of four v_mfma_f32_16x16x32_bf16, so each reconstructed
+//     weight is used straight from registers and never stored;
 //   - codes are prefetched two steps ahead; all loads are unconditional so the
 //     compiler's wait counts stay exact;
 //   - SwiGLU is applied to the gate/up accumulators before h is stored (gate
@@ -28,8 +28,9 @@
 //
 // MFMA operand convention: for the 16x16x32 bf16 MFMA, lane l supplies row
 // (l mod 16) of A and column (l mod 16) of B with eight consecutive reduction
-// elements; in MFMA j of a step, lane l carries inputs 32*(l/16) + 8*j .. +7
-// for both operands.  Lane l receives D rows 4*(l/16)+i, column l mod 16.
+// elements; in MFMA j of a step, lane l carries inputs 32*j + 8*(l/16) .. +7
+// for both operands, so MFMAs 0, 1 cover the step's first input group and
+// MFMAs 2, 3 its second.  Lane l receives D rows 4*(l/16)+i, column l mod 16.
 #include "route.h"
 
 namespace moe {
@@ -37,24 +38,26 @@ namespace moe {
 constexpr int kLDA = kKS + 8;     // LDS row pitch in bf16 (16-byte pad against bank conflicts)
 constexpr int kSmallM = 32;       // tiles up to this height go to the small-tile kernel
 
-// Raw operands of one step for one 16-row slice: 16 code bytes and the packed
-// (scale, bias) dword.
+// Raw operands of one step for one 16-row slice: the lane's four code words
+// (word j for MFMA j) and the (scale, bias) dwords of its row for the step's
+// two input groups.
 struct SliceOps {
   uint4 q;
-  uint32_t sb;
+  uint2 sb;
 };
 
 __device__ __forceinline__ void load_slice(const uint8_t* blk, int lane, SliceOps& o) {
   o.q = *reinterpret_cast<const uint4*>(blk + lane * 16);
-  o.sb = *reinterpret_cast<const uint32_t*>(blk + kPackScales + (((lane >> 5) << 4) + (lane & 15)) * 4);
+  o.sb = *reinterpret_cast<const uint2*>(blk + kPackScales + (lane & 15) * 8);
 }
 
 __device__ __forceinline__ void rebuild_slice(const SliceOps& o, bf16x8 (&b)[4]) {
-  const float sc = bf16_to_f32(o.sb & 0xFFFFu), bi = bf16_to_f32(o.sb >> 16);
-  b[0] = as_bf16x8(dequant8(o.q.x, sc, bi));
-  b[1] = as_bf16x8(dequant8(o.q.y, sc, bi));
-  b[2] = as_bf16x8(dequant8(o.q.z, sc, bi));
-  b[3] = as_bf16x8(dequant8(o.q.w, sc, bi));
+  const float s0 = bf16_to_f32(o.sb.x & 0xFFFFu), b0 = bf16_to_f32(o.sb.x >> 16);
+  const float s1 = bf16_to_f32(o.sb.y & 0xFFFFu), b1 = bf16_to_f32(o.sb.y >> 16);
+  b[0] = as_bf16x8(dequant8_pairs(o.q.x, s0, b0));
+  b[1] = as_bf16x8(dequant8_pairs(o.q.y, s0, b0));
+  b[2] = as_bf16x8(dequant8_pairs(o.q.z, s1, b1));
+  b[3] = as_bf16x8(dequant8_pairs(o.q.w, s1, b1));
 }
 
 // Common per-workgroup setup: block entry, validation, the bank's packed matrix.
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int n = lane & 15;
-  const int lk = (lane >> 4) * 32;
+  const int lk = (lane >> 4) * 8;
   const int mtiles = bi.tm >> 4;
   const int row0 = bi.row0, rows = bi.rows;
 
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
           const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk];
           bf16x8 af[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 8);
+          for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 32);
 #pragma unroll
           for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
@@ -385,44 +388,39 @@ __device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& b
     }
   };
   // Lane l reads column n = l mod 32 of the tile, i.e. row n mod 16 of slice
-  // n/16.  In the packed block, the inputs 32p .. 32p+31 of that row are the
-  // 16 bytes at (16p + row) * 16; k-chunk j (inputs 16j + 8h .., h = l/32) is
-  // word 2 (j mod 2) + h of chunk p = j/2.  The codes of a step are read in
-  // one asm block that ends with its own lgkmcnt wait: the compiler cannot
-  // tell which of the copies in flight such reads depend on and would
-  // otherwise wait for all of them; the explicit vmcnt waits before each call
-  // cover the copies they need.
+  // n/16.  k-chunk j holds inputs 16j + 8h .. +7 (h = l/32) of that row: in
+  // the packed block, word j/2 of the 16 bytes at (16 (2 (j mod 2) + h) +
+  // row) * 16, so the step's codes are two 16-byte reads, and the row's two
+  // scale/bias words are adjacent.  The codes of a step are read in one asm
+  // block that ends with its own lgkmcnt wait: the compiler cannot tell which
+  // of the copies in flight such reads depend on and would otherwise wait for
+  // all of them; the explicit vmcnt waits before each call cover the copies
+  // they need.
   const int h = lane >> 5, nrow = lane & 15, nsl = (lane >> 4) & 1;
   auto read_codes = [&](const uint8_t* cbuf, TileCodes& tc) {
     const uint8_t* slot = cbuf + cw + nsl * kCodeSlot;
-    const uint32_t ac = lds_addr(slot + nrow * 16);
-    const uint32_t as = lds_addr(slot + kPackScales + (nrow >> 2) * 16);
-    u32x4 c[4], g[2];
+    const uint32_t ac = lds_addr(slot + (16 * h + nrow) * 16);
+    const uint32_t as = lds_addr(slot + kPackScales + nrow * 8);
+    u32x4 ce, co;
+    u32x2 g;
     asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:256\n\t"
-        "ds_read_b128 %2, %6 offset:512\n\t"
-        "ds_read_b128 %3, %6 offset:768\n\t"
-        "ds_read_b128 %4, %7\n\t"
-        "ds_read_b128 %5, %7 offset:64\n\t"
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %3 offset:512\n\t"
+        "ds_read_b64 %2, %4\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(g[0]), "=&v"(g[1])
+        : "=&v"(ce), "=&v"(co), "=&v"(g)
         : "v"(ac), "v"(as));
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      tc.q[2 * p] = h ? c[p].y : c[p].x;
-      tc.q[2 * p + 1] = h ? c[p].w : c[p].z;
-    }
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const uint32_t lo = (nrow & 1) ? g[gg].y : g[gg].x, hi = (nrow & 1) ? g[gg].w : g[gg].z;
-      tc.sb[gg] = (nrow & 2) ? hi : lo;
-    }
+    tc.q[0] = ce.x; tc.q[1] = co.x;
+    tc.q[2] = ce.y; tc.q[3] = co.y;
+    tc.q[4] = ce.z; tc.q[5] = co.z;
+    tc.q[6] = ce.w; tc.q[7] = co.w;
+    tc.sb[0] = g.x;
+    tc.sb[1] = g.y;
   };
   // weights of k-chunk j of the tile
   auto rebuild_j = [&](const TileCodes& tc, int j) -> bf16x8 {
     const uint32_t sbw = tc.sb[j >> 2];
-    return as_bf16x8(dequant8(tc.q[j], bf16_to_f32(sbw & 0xFFFFu), bf16_to_f32(sbw >> 16)));
+    return as_bf16x8(dequant8_pairs(tc.q[j], bf16_to_f32(sbw & 0xFFFFu), bf16_to_f32(sbw >> 16)));
   };
   // LDS byte offset of this lane's A fragment for k-chunk j within a 32-row tile
   const int arow_l = lane & 31;
@@ -624,7 +622,7 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   // Rows past the block read the block's last row: an MFMA row only reaches
   // its own output row, and those are never stored.
   const uint16_t* arow = src + static_cast<size_t>(srow) * K;
-  const int kq = (lane >> 4) * 32;
+  const int kq = (lane >> 4) * 8;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto chunk = [&](int s0, const SliceOps (&o)[kGemvChunk]) {
@@ -634,7 +632,7 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
       const int s = min(s0 + u, s_end - 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        av[u][j] = *reinterpret_cast<const uint4*>(arow + min(s * kKS + kq + 8 * j, K - 8));
+        av[u][j] = *reinterpret_cast<const uint4*>(arow + min(s * kKS + 32 * j + kq, K - 8));
     }
 #pragma unroll
     for (int u = 0; u < kGemvChunk; ++u) {
@@ -645,7 +643,7 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
       rebuild_slice(o[u], b);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + kq + 8 * j < K) ? ~0u : 0u;
+        uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + 32 * j + kq < K) ? ~0u : 0u;
         asm("" : "+v"(mk));
         const uint4 v = make_uint4(av[u][j].x & mk, av[u][j].y & mk, av[u][j].z & mk, av[u][j].w & mk);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v), b[j], acc, 0, 0, 0);

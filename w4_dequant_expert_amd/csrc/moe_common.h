@@ -13,6 +13,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -63,6 +64,29 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b) {
   return r;
 }
 
+// dequant8 for a code word in pair order (as stored in the packed layout):
+// the same eight weights, in element order.
+__device__ __forceinline__ uint4 dequant8_pairs(uint32_t w, float s, float b) {
+  uint32_t ev = w & 0x0F0F0F0Fu;          // elements 0, 4, 1, 5 (bytes 0..3)
+  uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // elements 2, 6, 3, 7
+  asm("" : "+v"(ev));
+  asm("" : "+v"(od));
+  const float f0 = __builtin_fmaf(static_cast<float>(ev & 0xFFu), s, b);
+  const float f4 = __builtin_fmaf(static_cast<float>((ev >> 8) & 0xFFu), s, b);
+  const float f1 = __builtin_fmaf(static_cast<float>((ev >> 16) & 0xFFu), s, b);
+  const float f5 = __builtin_fmaf(static_cast<float>(ev >> 24), s, b);
+  const float f2 = __builtin_fmaf(static_cast<float>(od & 0xFFu), s, b);
+  const float f6 = __builtin_fmaf(static_cast<float>((od >> 8) & 0xFFu), s, b);
+  const float f3 = __builtin_fmaf(static_cast<float>((od >> 16) & 0xFFu), s, b);
+  const float f7 = __builtin_fmaf(static_cast<float>(od >> 24), s, b);
+  uint4 r;
+  r.x = pack_bf16x2(f0, f1);
+  r.y = pack_bf16x2(f2, f3);
+  r.z = pack_bf16x2(f4, f5);
+  r.w = pack_bf16x2(f6, f7);
+  return r;
+}
+
 // Wave-uniform copy of a value the compiler cannot prove uniform.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -78,18 +102,21 @@ __device__ __forceinline__ void status_set(uint32_t* status, uint32_t bits) {
 // A matrix of N output rows and K inputs is cut into N/16 slices of 16 rows
 // and ceil(K/128) steps of 128 inputs.  Each (slice, step) is one contiguous
 // block of kPackBlock bytes, blocks ordered slice-major:
-//   bytes [0, 1024): lane l (0..63) of a wave finds at l*16 the 16 code bytes
-//     (32 consecutive inputs step*128 + (l/16)*32 ..) of row (l mod 16) of the
-//     slice, in the canonical nibble order;
-//   bytes [1024, 1152): 32 dwords; dword g*16 + r holds the scale (low half)
+//   bytes [0, 1024): lane l (0..63) of a wave finds at l*16 four code words
+//     of row (l mod 16) of the slice; word j holds the eight inputs
+//     step*128 + 32j + 8*(l/16) .. +7, in pair order (below);
+//   bytes [1024, 1152): 32 dwords; dword 2r + g holds the scale (low half)
 //     and bias (high half) of row r for inputs step*128 + g*64 .. +63.
+// Pair order: nibble t of a code word holds element 2t and nibble t+4 holds
+// element 2t+1 (t = 0..3), so that masking the word shifted by 4t with
+// 0x000F000F puts elements 2t and 2t+1 in the two halves of one dword.
 // Inputs past K are code 0 with scale 0 and bias 0 (they rebuild to +0).
 // Gate/up matrices interleave gate and up rows: slice c holds gate rows
 // 8c..8c+7 as rows 0..7 and the matching up rows I+8c.. as rows 8..15, so a
 // lane's gate and up outputs sit 8 lanes apart.  Down matrices are straight:
 // slice c holds rows 16c..16c+15.
-// Every wave load is a whole 1024-byte (or 128-byte) run and every byte is
-// read once per use, which is what lets the GEMMs stream at HBM speed.
+// A 16x16x32 MFMA over inputs 32j .. 32j+31 of a step takes word j of every
+// lane as its B operand; both of the step's scale groups are whole MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kKS = 128;             // inputs per step
 constexpr int kPackBlock = 1152;     // bytes per (slice, step) block

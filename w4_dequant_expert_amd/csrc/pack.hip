@@ -9,7 +9,7 @@
 
 namespace moe {
 
-// One thread per (matrix, slice, step, lane): 16 code bytes, plus one
+// One thread per (matrix, slice, step, lane): four code words, plus one
 // (scale, bias) dword for the even lane groups.
 __global__ __launch_bounds__(256) void pack_kernel(int nmat, int N, int K, int gate_up,
                                                    const uint8_t* __restrict__ q,
@@ -36,10 +36,22 @@ __global__ __launch_bounds__(256) void pack_kernel(int nmat, int N, int K, int g
   uint8_t* blk = out + static_cast<size_t>(mat) * pack_bytes(N, K) +
                  (static_cast<size_t>(slice) * nk + step) * kPackBlock;
 
-  const int k0 = step * kKS + g * 32;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (k0 < K) v = *reinterpret_cast<const uint4*>(qm + static_cast<size_t>(row) * (K / 2) + k0 / 2);
-  *reinterpret_cast<uint4*>(blk + lane * 16) = v;
+  // word j: inputs step*128 + 32j + 8g .. +7, nibbles regrouped in pair order
+  uint32_t wv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k0 = step * kKS + 32 * j + 8 * g;
+    uint32_t c = 0;
+    if (k0 < K) c = *reinterpret_cast<const uint32_t*>(qm + static_cast<size_t>(row) * (K / 2) + k0 / 2);
+    uint32_t p = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+      p |= ((c >> (4 * e)) & 0xFu) << (4 * pos);
+    }
+    wv[j] = p;
+  }
+  *reinterpret_cast<uint4*>(blk + lane * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   if ((g & 1) == 0) {
     const int gg = g >> 1;                 // group of the step: inputs gg*64 .. +63
     const int grp = step * 2 + gg;
@@ -48,7 +60,7 @@ __global__ __launch_bounds__(256) void pack_kernel(int nmat, int N, int K, int g
       const size_t gi = static_cast<size_t>(row) * (K / 64) + grp;
       sb = static_cast<uint32_t>(sm[gi]) | (static_cast<uint32_t>(bm[gi]) << 16);
     }
-    *reinterpret_cast<uint32_t*>(blk + kPackScales + (gg * 16 + r) * 4) = sb;
+    *reinterpret_cast<uint32_t*>(blk + kPackScales + (2 * r + gg) * 4) = sb;
   }
 }
 
