@@ -5,6 +5,8 @@ import ctypes
 import os
 import re
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 import pytest
 
 import w4_dequant_expert_amd as moe
@@ -30,7 +32,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert moe.moe_abi_version() == 1
+    header = open(os.path.join(ROOT, "include", "moe_w4.h")).read()
+    m = re.search(r"#define MOE_W4_ABI_VERSION (\d+)", header)
+    assert m and moe.moe_abi_version() == int(m.group(1))
     for code in (0, -1, -2, -3, -4, -5):
         assert moe.strerror(code) and moe.strerror(code) != "unknown error"
 

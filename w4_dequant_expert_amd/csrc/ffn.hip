@@ -51,13 +51,77 @@ __device__ __forceinline__ void load_slice(const uint8_t* blk, int lane, SliceOp
   o.sb = *reinterpret_cast<const uint2*>(blk + kPackScales + (lane & 15) * 8);
 }
 
-__device__ __forceinline__ void rebuild_slice(const SliceOps& o, bf16x8 (&b)[4]) {
-  const float s0 = bf16_to_f32(o.sb.x & 0xFFFFu), b0 = bf16_to_f32(o.sb.x >> 16);
-  const float s1 = bf16_to_f32(o.sb.y & 0xFFFFu), b1 = bf16_to_f32(o.sb.y >> 16);
-  b[0] = as_bf16x8(dequant8_pairs(o.q.x, s0, b0));
-  b[1] = as_bf16x8(dequant8_pairs(o.q.y, s0, b0));
-  b[2] = as_bf16x8(dequant8_pairs(o.q.z, s1, b1));
-  b[3] = as_bf16x8(dequant8_pairs(o.q.w, s1, b1));
+// Scale after the product.  Within one input group g of a weight row,
+//   sum_k a_k (q_k s + b) = s * sum_k a_k (128 + q_k) + (b - 128 s) * sum_k a_k,
+// and 128 + q (q = 0..15) is a bfloat16 with the code in its low mantissa
+// bits: OR-ing the two codes of a pair-order nibble pair into 0x4300 (128.0)
+// gives the MFMA operand with two VALU operations per pair of weights.  The
+// matrix core then forms P = sum a (128 + q) and X = sum a (a ones operand)
+// per group, and two float32 FMAs per output apply the group's scale and
+// bias.  This replaces the per-weight convert, FMA and round of a rebuild
+// whenever a rebuilt weight would feed only one or two 16-row tiles.
+// The identity is exact; the float32 products and sums round differently
+// from a bfloat16 rebuild, well inside the layer's tolerance (X and P are
+// exact products summed in float32, and |P s| exceeds the result by about the
+// ratio 128 / |q - 8| at most).
+// The mask and the exponent pattern are passed in registers: with literal
+// constants the compiler splits each v_and_or_b32 into an AND and an OR.
+struct PairConsts {
+  uint32_t mask, magic;
+};
+
+__device__ __forceinline__ PairConsts pair_consts() {
+  PairConsts k{0x000F000Fu, 0x43004300u};
+  asm("" : "+v"(k.mask));
+  asm("" : "+v"(k.magic));
+  return k;
+}
+
+__device__ __forceinline__ bf16x8 codes_plus128(uint32_t w, const PairConsts& k) {
+  u32x4 r;
+  r.x = (w & k.mask) | k.magic;
+  r.y = ((w >> 4) & k.mask) | k.magic;
+  r.z = ((w >> 8) & k.mask) | k.magic;
+  r.w = ((w >> 12) & k.mask) | k.magic;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// MFMA operand of eight bfloat16 ones.
+__device__ __forceinline__ bf16x8 bf16_ones() {
+  const u32x4 r = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Sum of the eight bfloat16 values of a 16-byte chunk, in float32.
+__device__ __forceinline__ float sum8_bf16(uint4 v) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), one, 0.0f, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), one, d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), one, d, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), one, d, false);
+}
+
+// Value of another lane through a DPP lane pattern (CTRL: quad_perm or row
+// mirror encoding).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of eight lanes (lane xor 1, xor 2, then the
+// mirror inside the half row, which pairs the two quads).
+__device__ __forceinline__ float sum_lanes8(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  return v;
+}
+
+// Scale s and the folded bias b - 128 s of a packed (scale, bias) dword.
+__device__ __forceinline__ void group_affine(uint32_t sb, float& s, float& c) {
+  s = __uint_as_float(sb << 16);
+  c = __builtin_fmaf(-128.0f, s, __uint_as_float(sb & 0xFFFF0000u));
 }
 
 // Common per-workgroup setup: block entry, validation, the bank's packed matrix.
@@ -123,20 +187,19 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 
 // ---------------------------------------------------------------------------
 // Small-tile kernel: blocks of at most 32 rows.  Eight waves, two slices each
-// (a workgroup covers 16 slices), one A chunk per thread per step.
+// (a workgroup covers 16 slices of one block), one A chunk per thread per
+// step.
 // ---------------------------------------------------------------------------
+// Group sums of the staged activations: Xs[buf][g][copy][row], eight copies
+// (one per lane of a group) so that every lane stores unconditionally.
+constexpr int kXsWords = 2 * 2 * 8 * kSmallM;
+
 template <bool GATE_UP>
-__global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
-                                                            const uint16_t* __restrict__ src,
-                                                            uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
-  __shared__ int s_tok[kSmallM];
-
-  BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi)) return;
-  if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
-  if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
-
+__device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
+                                            const uint16_t* __restrict__ src,
+                                            uint16_t* __restrict__ out,
+                                            uint16_t (*As)[kSmallM * kLDA], float* Xs,
+                                            const int* s_tok) {
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int nk = pack_steps(K);
@@ -156,11 +219,6 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
     sbase[sl] = bi.P + static_cast<size_t>(sl_on[sl] ? c : 0) * nk * kPackBlock;
   }
   const bool active = sl_on[0];
-
-  if (GATE_UP) {
-    block_tokens(a, bi, s_tok);
-    __syncthreads();
-  }
 
   // A staging: tm rows x 16 chunks of 16 bytes, one chunk per thread; rows
   // past the block read row 0 and are zeroed
@@ -182,6 +240,8 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
     // am < kSmallM always: unconditional, so no divergent branch disturbs the
     // wait counts of the code prefetch
     *reinterpret_cast<uint4*>(&As[buf][am * kLDA + ac * 8]) = v;
+    // the row's sum over the chunk's input group (eight lanes hold a group)
+    Xs[((buf * 2 + (ac >> 3)) * 8 + (ac & 7)) * kSmallM + am] = sum_lanes8(sum8_bf16(v));
   };
   // steps past the end reload the last step (never used): no branch
   auto load_codes = [&](int s, SliceOps (&o)[2]) {
@@ -196,27 +256,51 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Per step: operands 128 + q of both slices and their groups' affine
+  // terms; per 16-row tile and group, X = sum a over the group (staged with
+  // the activations), then P per slice and the scale-after update.
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const PairConsts pk = pair_consts();
   auto step = [&](int s, SliceOps (&o)[2], int buf, uint4& ar) {
-    bf16x8 bfr[2][4];
-    if (active) {
+    // this step's codes leave the prefetch registers before the next load
+    uint32_t qw[2][4];
+    float gs[2][2], gc[2][2];
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) rebuild_slice(o[sl], bfr[sl]);
+    for (int sl = 0; sl < 2; ++sl) {
+      qw[sl][0] = o[sl].q.x;
+      qw[sl][1] = o[sl].q.y;
+      qw[sl][2] = o[sl].q.z;
+      qw[sl][3] = o[sl].q.w;
+      group_affine(o[sl].sb.x, gs[sl][0], gc[sl][0]);
+      group_affine(o[sl].sb.y, gs[sl][1], gc[sl][1]);
     }
     load_codes(s + 2, o);
     if (active) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < mtiles) {
-          const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk];
-          bf16x8 af[4];
+      for (int g = 0; g < 2; ++g) {
+        bf16x8 bq[2][2];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(ap + j * 32);
+        for (int sl = 0; sl < 2; ++sl) {
+          bq[sl][0] = codes_plus128(qw[sl][2 * g], pk);
+          bq[sl][1] = codes_plus128(qw[sl][2 * g + 1], pk);
+        }
 #pragma unroll
-          for (int sl = 0; sl < 2; ++sl)
+        for (int mt = 0; mt < 2; ++mt) {
+          if (mt < mtiles) {
+            const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk + 64 * g];
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 32);
+            const f32x4 X = *reinterpret_cast<const f32x4*>(
+                &Xs[((buf * 2 + g) * 8) * kSmallM + mt * 16 + 4 * (lane >> 4)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[mt][sl] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfr[sl][j], acc[mt][sl], 0, 0, 0);
+            for (int sl = 0; sl < 2; ++sl) {
+              f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
+              P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq[sl][1], P, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[mt][sl][i] = __builtin_fmaf(P[i], gs[sl][g], __builtin_fmaf(X[i], gc[sl][g], acc[mt][sl][i]));
+            }
+          }
         }
       }
     }
@@ -261,6 +345,24 @@ __global__ __launch_bounds__(512) void w4_gemm_small_kernel(GemmArgs a,
       }
     }
   }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
+  __shared__ __attribute__((aligned(16))) float Xs[kXsWords];
+  __shared__ int s_tok[kSmallM];
+
+  BlockInfo bi;
+  if (!block_info<GATE_UP>(a, bi)) return;
+  if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
+  if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
+  if (GATE_UP) {
+    block_tokens(a, bi, s_tok);
+    __syncthreads();
+  }
+  small_block<GATE_UP>(a, bi, src, out, As, Xs, s_tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -625,6 +727,9 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   const int kq = (lane >> 4) * 8;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = bf16_ones();
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const PairConsts pk = pair_consts();
   auto chunk = [&](int s0, const SliceOps (&o)[kGemvChunk]) {
     uint4 av[kGemvChunk][4];
 #pragma unroll
@@ -638,15 +743,28 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
     for (int u = 0; u < kGemvChunk; ++u) {
       // Steps past the wave's range and inputs past K multiply zeros (the
       // mask is opaque to the compiler, so the loads above stay unconditional
-      // and their wait counts exact); the weights there are finite.
-      bf16x8 b[4];
-      rebuild_slice(o[u], b);
+      // and their wait counts exact); the weights there are finite.  Scale
+      // after the product, as in the small-tile kernel.
+      const uint32_t qw[4] = {o[u].q.x, o[u].q.y, o[u].q.z, o[u].q.w};
+      float gs[2], gc[2];
+      group_affine(o[u].sb.x, gs[0], gc[0]);
+      group_affine(o[u].sb.y, gs[1], gc[1]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + 32 * j + kq < K) ? ~0u : 0u;
-        asm("" : "+v"(mk));
-        const uint4 v = make_uint4(av[u][j].x & mk, av[u][j].y & mk, av[u][j].z & mk, av[u][j].w & mk);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v), b[j], acc, 0, 0, 0);
+      for (int g = 0; g < 2; ++g) {
+        bf16x8 am[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * g + jj;
+          uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + 32 * j + kq < K) ? ~0u : 0u;
+          asm("" : "+v"(mk));
+          am[jj] = as_bf16x8(make_uint4(av[u][j].x & mk, av[u][j].y & mk, av[u][j].z & mk, av[u][j].w & mk));
+        }
+        f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[0], ones, zero, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[1], ones, X, 0, 0, 0);
+        f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[0], codes_plus128(qw[2 * g], pk), zero, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[1], codes_plus128(qw[2 * g + 1], pk), P, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(P[i], gs[g], __builtin_fmaf(X[i], gc[g], acc[i]));
       }
     }
   };
