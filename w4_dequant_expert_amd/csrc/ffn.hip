@@ -7,24 +7,25 @@
 // expanded bfloat16 array is never written to memory.
 //
 // Work decomposition: one workgroup = one block of the block map x one N tile
-// (128 h columns for gate/up, 256 output columns for down).  Within it:
+// (a run of 16-row weight slices).  Within it:
 //   - the block's activation rows (gathered through sorted_slot for gate/up,
 //     contiguous h rows for down) are staged in LDS, 128 inputs at a time,
-//     double-buffered, and shared by all waves of the workgroup;
+//     and shared by all waves of the workgroup;
 //   - each wave owns whole 16-row weight slices; a lane loads 16 bytes of
 //     packed codes (four runs of 8 inputs of one weight row) plus the scale
-//     and bias of the step's two groups and rebuilds them in registers as the
-//     B operands of four v_mfma_f32_16x16x32_bf16, so each reconstructed
-//     weight is used straight from registers and never stored;
-//   - codes are prefetched two steps ahead; all loads are unconditional so the
+//     and bias of the step's two groups, and the codes become MFMA B operands
+//     in registers, so no reconstructed weight is ever stored;
+//   - codes are prefetched ahead; all loads are unconditional so the
 //     compiler's wait counts stay exact;
 //   - SwiGLU is applied to the gate/up accumulators before h is stored (gate
 //     and up outputs of a column are 8 lanes apart in the packed slices).
-// Two kernels share this scheme: a small-tile kernel (blocks of <= 32 rows,
-// eight light waves, high occupancy: streaming-bound work) and a tall-tile
-// kernel (blocks of 48..128 rows, four waves holding 128-row accumulators:
-// matrix-unit-bound work).  Each skips the blocks the other owns, so the host
-// launches both without knowing the routing.
+// Three kernels share this scheme: a small-tile kernel (blocks of <= 32 rows,
+// high occupancy, the scale applied after the product: streaming-bound work),
+// a tall-tile kernel (blocks of 48..128 rows, waves holding 128-row
+// accumulators over rebuilt bf16 weights: matrix-unit-bound work) and a
+// short-batch kernel for at most 16 tokens.  The small and tall kernels each
+// skip the blocks the other owns, so the host launches both without knowing
+// the routing.
 //
 // MFMA operand convention: for the 16x16x32 bf16 MFMA, lane l supplies row
 // (l mod 16) of A and column (l mod 16) of B with eight consecutive reduction
@@ -37,6 +38,10 @@ namespace moe {
 
 constexpr int kLDA = kKS + 8;     // LDS row pitch in bf16 (16-byte pad against bank conflicts)
 constexpr int kSmallM = 32;       // tiles up to this height go to the small-tile kernel
+// Waves (two slices each) per small-tile workgroup.  Four waves give four
+// workgroups per CU at the kernel's register budget, the same sixteen waves
+// as two eight-wave workgroups but with finer-grained scheduling.
+constexpr int kSmallWaves = 4;
 
 // Raw operands of one step for one 16-row slice: the lane's four code words
 // (word j for MFMA j) and the (scale, bias) dwords of its row for the step's
@@ -138,9 +143,16 @@ struct BlockInfo {
 // holds ceil(blocks / 8) * 8 * ntiles workgroups.
 constexpr int kXcds = 8;
 
+// N tiles of a block when a workgroup covers spw slices.
 template <bool GATE_UP>
-__device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi) {
-  const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
+__host__ __device__ inline int n_tiles(const GemmArgs& a, int spw) {
+  const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
+  return (nslices + spw - 1) / spw;
+}
+
+template <bool GATE_UP>
+__device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi, int spw) {
+  const int ntiles = n_tiles<GATE_UP>(a, spw);
   const int r = blockIdx.x / kXcds;
   const int bid = kXcds * (r / ntiles) + blockIdx.x % kXcds;
   bi.nt = r % ntiles;
@@ -186,15 +198,15 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 }
 
 // ---------------------------------------------------------------------------
-// Small-tile kernel: blocks of at most 32 rows.  Eight waves, two slices each
-// (a workgroup covers 16 slices of one block), one A chunk per thread per
-// step.
+// Small-tile kernel: blocks of at most 32 rows.  WAVES waves, two slices
+// each (a workgroup covers 2 WAVES slices of one block); each thread stages
+// 32 * 16 / (64 WAVES) activation chunks per step.
 // ---------------------------------------------------------------------------
 // Group sums of the staged activations: Xs[buf][g][copy][row], eight copies
 // (one per lane of a group) so that every lane stores unconditionally.
 constexpr int kXsWords = 2 * 2 * 8 * kSmallM;
 
-template <bool GATE_UP>
+template <int WAVES, bool GATE_UP>
 __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
@@ -214,34 +226,48 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   const uint8_t* sbase[2];  // slice's first block
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
-    const int c = bi.nt * 16 + wave * 2 + sl;
+    const int c = bi.nt * (2 * WAVES) + wave * 2 + sl;
     sl_on[sl] = c < nslices;
     sbase[sl] = bi.P + static_cast<size_t>(sl_on[sl] ? c : 0) * nk * kPackBlock;
   }
   const bool active = sl_on[0];
 
-  // A staging: tm rows x 16 chunks of 16 bytes, one chunk per thread; rows
-  // past the block read row 0 and are zeroed
-  const int am = tid >> 4, ac = tid & 15;
-  bool a_ok = am < rows;
-  const uint16_t* arow;
-  if (GATE_UP) {
-    const int tok = a_ok ? s_tok[am] : -1;
-    a_ok = tok >= 0;
-    arow = src + static_cast<size_t>(a_ok ? tok : 0) * K;
-  } else {
-    arow = src + static_cast<size_t>(row0 + (a_ok ? am : 0)) * K;
+  // A staging: tm rows x 16 chunks of 16 bytes, NPASS chunks per thread
+  // (rows am, am + 4 WAVES, ...); rows past the block read row 0 and are zeroed
+  constexpr int NPASS = kSmallM * 16 / (64 * WAVES);
+  const int ac = tid & 15;
+  int am[NPASS];
+  bool a_ok[NPASS];
+  const uint16_t* arow[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    am[p] = (tid >> 4) + p * 4 * WAVES;
+    a_ok[p] = am[p] < rows;
+    if (GATE_UP) {
+      const int tok = a_ok[p] ? s_tok[am[p]] : -1;
+      a_ok[p] = tok >= 0;
+      arow[p] = src + static_cast<size_t>(a_ok[p] ? tok : 0) * K;
+    } else {
+      arow[p] = src + static_cast<size_t>(row0 + (a_ok[p] ? am[p] : 0)) * K;
+    }
   }
-  auto load_a = [&](int s) -> uint4 {
-    return *reinterpret_cast<const uint4*>(arow + min(s * kKS + ac * 8, K - 8));
+  typedef uint4 AChunks[NPASS];
+  auto load_a = [&](int s, AChunks& v) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+      v[p] = *reinterpret_cast<const uint4*>(arow[p] + min(s * kKS + ac * 8, K - 8));
   };
-  auto store_a = [&](int buf, uint4 v, int s) {
-    if (!(a_ok && s < nk && s * kKS + ac * 8 < K)) v = make_uint4(0, 0, 0, 0);
-    // am < kSmallM always: unconditional, so no divergent branch disturbs the
-    // wait counts of the code prefetch
-    *reinterpret_cast<uint4*>(&As[buf][am * kLDA + ac * 8]) = v;
-    // the row's sum over the chunk's input group (eight lanes hold a group)
-    Xs[((buf * 2 + (ac >> 3)) * 8 + (ac & 7)) * kSmallM + am] = sum_lanes8(sum8_bf16(v));
+  auto store_a = [&](int buf, const AChunks& ar, int s) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      uint4 v = ar[p];
+      if (!(a_ok[p] && s < nk && s * kKS + ac * 8 < K)) v = make_uint4(0, 0, 0, 0);
+      // am < kSmallM always: unconditional, so no divergent branch disturbs
+      // the wait counts of the code prefetch
+      *reinterpret_cast<uint4*>(&As[buf][am[p] * kLDA + ac * 8]) = v;
+      // the row's sum over the chunk's input group (eight lanes hold a group)
+      Xs[((buf * 2 + (ac >> 3)) * 8 + (ac & 7)) * kSmallM + am[p]] = sum_lanes8(sum8_bf16(v));
+    }
   };
   // steps past the end reload the last step (never used): no branch
   auto load_codes = [&](int s, SliceOps (&o)[2]) {
@@ -261,7 +287,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   // the activations), then P per slice and the scale-after update.
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const PairConsts pk = pair_consts();
-  auto step = [&](int s, SliceOps (&o)[2], int buf, uint4& ar) {
+  auto step = [&](int s, SliceOps (&o)[2], int buf, AChunks& ar) {
     // this step's codes leave the prefetch registers before the next load
     uint32_t qw[2][4];
     float gs[2][2], gc[2][2];
@@ -305,16 +331,17 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
       }
     }
     store_a(buf ^ 1, ar, s + 1);
-    ar = load_a(s + 2);
+    load_a(s + 2, ar);
     __syncthreads();
   };
 
   SliceOps c0[2], c1[2];
   load_codes(0, c0);
   load_codes(1, c1);
-  uint4 ar = load_a(0);
+  AChunks ar;
+  load_a(0, ar);
   store_a(0, ar, 0);
-  ar = load_a(1);
+  load_a(1, ar);
   __syncthreads();
   for (int s = 0; s < nk; s += 2) {
     step(s, c0, 0, ar);
@@ -331,7 +358,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
       const size_t r = static_cast<size_t>(row0 + m);
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
-        const int c = bi.nt * 16 + wave * 2 + sl;
+        const int c = bi.nt * (2 * WAVES) + wave * 2 + sl;
         const float v = acc[mt][sl][i];
         if (GATE_UP) {
           const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
@@ -347,22 +374,22 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   }
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
+template <int WAVES, bool GATE_UP>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
     GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
   __shared__ __attribute__((aligned(16))) float Xs[kXsWords];
   __shared__ int s_tok[kSmallM];
 
   BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi)) return;
+  if (!block_info<GATE_UP>(a, bi, 2 * WAVES)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
   if (GATE_UP) {
     block_tokens(a, bi, s_tok);
     __syncthreads();
   }
-  small_block<GATE_UP>(a, bi, src, out, As, Xs, s_tok);
+  small_block<WAVES, GATE_UP>(a, bi, src, out, As, Xs, s_tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -637,7 +664,7 @@ __global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
   __shared__ int s_tok[kTallM];
 
   BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi)) return;
+  if (!block_info<GATE_UP>(a, bi, 2 * kTallWaves)) return;
   if (bi.tm <= kSmallM) return;  // a short block: the small-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
   if (GATE_UP) {
@@ -829,12 +856,14 @@ template <bool GATE_UP>
 static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src, uint16_t* out,
                               hipStream_t stream) {
   if (a.T <= kGemvRows) return launch_gemv<GATE_UP>(a, src, out, stream);
-  const int ntiles = GATE_UP ? (a.I + 127) / 128 : (a.H + 255) / 256;
   const long long blocks8 = (a.max_blocks + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid(static_cast<unsigned>(blocks8 * ntiles));
-  hipLaunchKernelGGL((w4_gemm_small_kernel<GATE_UP>), grid, dim3(512), 0, stream, a, src, out);
-  if (m_max)
+  const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kSmallWaves)));
+  hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, GATE_UP>), grid_small, dim3(64 * kSmallWaves), 0,
+                     stream, a, src, out);
+  if (m_max) {
+    const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kTallWaves)));
     hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, a, src, out);
+  }
   return hipGetLastError();
 }
 
