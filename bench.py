@@ -46,11 +46,12 @@ def parse():
     p.add_argument("--copies", type=int, default=4, help="weight copies rotated between steps")
     p.add_argument("--tile-m-max", type=int, default=None,
                    help="largest GEMM tile height (default: per workload)")
-    p.add_argument("--no-extra", action="store_true", help="skip the 2048-token and decode legs")
+    p.add_argument("--no-extra", action="store_true", help="skip the 2048-token, decode and chunked-prompt legs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration)")
-    p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1"], default=None,
+    p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1", "chunked16384"],
+                   default=None,
                    help="time a single workload (profiling runs)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
@@ -227,6 +228,54 @@ def decode_leg(copies=40):
     return out
 
 
+def chunked_leg(copies, reps=3):
+    """Long prompt: 16384 tokens as 8 independent layer calls of 2048 tokens
+    (route, gate/up, down, combine each), timed per chunk with HIP events over
+    `reps` passes; steady state is the median over chunks 2..8 of each chunk's
+    fastest pass.  Temporary device memory per chunk is the layer's scratch
+    (routing tables and workspace, h, y_slots), all allocated once up front;
+    the allocator's peak during the timed passes is reported beside it."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    from synth import CONFIGS, make_tokens
+    cfg = CONFIGS["chunked16384"]
+    chunk, n = cfg["chunk"], cfg["T"] // cfg["chunk"]
+    wl = Workload("chunked16384", copies, T=chunk)
+    xs = [torch.from_numpy(make_tokens(chunk, wl.sh.H, cfg["x_seed"], t0=c * chunk).view(np.int16))
+          .to("cuda") for c in range(n)]
+    for c in range(n):                       # warm-up pass
+        wl.step(c, x=xs[c])
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    ms = [[] for _ in range(n)]
+    for r in range(reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for c in range(n):
+            evs[c][0].record()
+            wl.step(n * (r + 1) + c, x=xs[c])
+            evs[c][1].record()
+        torch.cuda.synchronize()
+        for c in range(n):
+            ms[c].append(evs[c][0].elapsed_time(evs[c][1]))
+    best = [min(v) for v in ms]
+    steady = statistics.median(best[1:])
+    L = wl.layer
+    scratch = [t for t in vars(L.rt).values() if isinstance(t, torch.Tensor)] + [L.h, L.y_slots]
+    temp = sum(t.numel() * t.element_size() for t in scratch)
+    out = dict(tokens_per_s=chunk / (steady * 1e-3), chunk_tokens=chunk, chunks=n,
+               chunk_ms=[round(v, 4) for v in best], steady_chunk_ms=round(steady, 4),
+               temp_bytes_per_chunk=temp,
+               alloc_peak_during_chunks=torch.cuda.max_memory_allocated() - base,
+               weight_copies=copies)
+    del wl, xs
+    return out
+
+
 def traffic_record():
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -316,6 +365,9 @@ def main():
     if main_name == "decode1":  # profiling runs of the decode leg alone
         print(json.dumps({"decode1": decode_leg(40)}))
         return
+    if main_name == "chunked16384":
+        print(json.dumps({"chunked16384": chunked_leg(args.copies)}))
+        return
     wl = Workload(main_name, args.copies, args.tile_m_max)
     wall, stages = time_workload(wl, args.steps, args.warmup)
     work = wl.work()
@@ -347,6 +399,8 @@ def main():
         del wl2
         torch.cuda.empty_cache()
         extra["decode1"] = decode_leg(40)
+        torch.cuda.empty_cache()
+        extra["chunked16384"] = chunked_leg(args.copies)
         torch.cuda.empty_cache()
 
     out = {
