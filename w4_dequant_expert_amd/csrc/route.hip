@@ -187,7 +187,7 @@ __global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
 // (token, expert) then meet in LDS, where one thread applies the tree
 // p[i] += p[i+s], s = 32..1, and adds the bias.
 // ---------------------------------------------------------------------------
-constexpr int kShortHC = 1024;           // inputs of x staged per pass
+constexpr int kShortHC = 2048;           // inputs of x staged per pass
 constexpr int kShortIU = kShortHC / 64;  // chain steps per pass
 
 template <int TT>  // batch bucket: T <= TT; rows T..TT-1 are computed and dropped
@@ -217,17 +217,18 @@ __global__ __launch_bounds__(1024) void router_scores_short_kernel(
 #pragma unroll
     for (int i = 0; i < kShortIU; ++i)
       wv[i] = wr[static_cast<size_t>(c + min(i, ni - 1) * 64 + m) * E + ec];
-    // x[0..T)[c .. c + 64 ni) as bfloat16, 16 bytes per thread and pass
+    // x[0..T)[c .. c + 64 ni) as bfloat16, XU 16-byte chunks per thread and pass
+    constexpr int XU = (TT * kShortHC / 8 + 1023) / 1024;
     const int nq = T * ni * 8;
-    uint4 xv[2];
+    uint4 xv[XU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < XU; ++u) {
       const int q = min(tid + u * 1024, nq - 1);
       const int t = q / (ni * 8), cc = q % (ni * 8);
       xv[u] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + c + cc * 8);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < XU; ++u) {
       const int q = tid + u * 1024;
       if (q < nq) {
         const int t = q / (ni * 8), cc = q % (ni * 8);
@@ -248,18 +249,21 @@ __global__ __launch_bounds__(1024) void router_scores_short_kernel(
 #pragma unroll
   for (int t = 0; t < TT; ++t) ps[t][m][es] = acc[t];
   __syncthreads();
+  // The tree, one level at a time across the threads of partial m < s2:
+  // level s2 reads entries s2 .. 2 s2 - 1, which it does not write.
+#pragma unroll
+  for (int s2 = 32; s2 >= 1; s2 >>= 1) {
+    if (m < s2) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) ps[t][m][es] = ps[t][m][es] + ps[t][m + s2][es];
+    }
+    __syncthreads();
+  }
   if (tid < T * 16) {
     const int t = tid >> 4, j = tid & 15;
     const int eo = blockIdx.x * 16 + j;
-    float p[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) p[i] = ps[t][i][j];
-#pragma unroll
-    for (int s2 = 32; s2 >= 1; s2 >>= 1)
-#pragma unroll
-      for (int i = 0; i < s2; ++i) p[i] = p[i] + p[i + s2];
     if (eo < E) {
-      float l = p[0];
+      float l = ps[t][0][j];
       if (bias) l = l + bias[eo];
       logits[static_cast<size_t>(t) * E + eo] = l;
     }
