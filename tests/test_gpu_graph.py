@@ -30,7 +30,9 @@ def _layer(T, tile_m_max):
     return layer, sh
 
 
-@pytest.mark.parametrize("T,tile_m_max", [(1, 32), (48, 32)])
+# (256, 128): the shared expert's 256 rows make tall blocks, so both GEMM
+# kernels are in the captured graph.
+@pytest.mark.parametrize("T,tile_m_max", [(1, 32), (48, 32), (256, 128)])
 def test_graph_replays_match_eager(T, tile_m_max):
     print(f"case graph replay T={T}", flush=True)
     layer, sh = _layer(T, tile_m_max)
