@@ -41,8 +41,8 @@ TILE_M_MAX = {"prefill512": 32, "prefill2048_zipf": 128, "chunked16384": 128, "d
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--copies", type=int, default=4, help="weight copies rotated between steps")
     p.add_argument("--tile-m-max", type=int, default=None,
                    help="largest GEMM tile height (default: per workload)")
