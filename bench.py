@@ -96,24 +96,27 @@ class Workload:
         self.y = torch.empty((self.T, sh.H), dtype=torch.int16, device="cuda")
 
     def step(self, i, ev=None, x=None):
+        """One layer call: route, gate/up, down, combine.  Untimed steps go
+        through the library's grouped FFN call; timed steps call gate/up and
+        down separately so that each stage has its own events."""
         r, s, wr = self.copies[i % len(self.copies)]
         L = self.layer
         L.w_router = wr
         x = self.x if x is None else x
-        if ev is not None:
-            ev[0].record()
+        if ev is None:
+            d = L.route(x)
+            L.ffn(d, x, r, s)
+            L.combine(d, self.y)
+            return
+        ev[0].record()
         d = L.route(x)
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
         L.gate_up(d, x, r, s)
-        if ev is not None:
-            ev[2].record()
+        ev[2].record()
         L.down(d, r, s)
-        if ev is not None:
-            ev[3].record()
+        ev[3].record()
         L.combine(d, self.y)
-        if ev is not None:
-            ev[4].record()
+        ev[4].record()
 
     def work(self):
         """Algorithmic flops and bytes of one call, from the real routing counts."""
@@ -210,14 +213,15 @@ def decode_leg(copies=40):
     L.route(x0)
     gu_ms = graph_ms(lambda i: L.gate_up(d, x0, wl.copies[i][0], wl.copies[i][1]), copies)
     dn_ms = graph_ms(lambda i: L.down(d, wl.copies[i][0], wl.copies[i][1]), copies)
+    ffn_ms = graph_ms(lambda i: L.ffn(d, x0, wl.copies[i][0], wl.copies[i][1]), copies)
     cb_ms = graph_ms(lambda i: L.combine(d, wl.y), copies)
     wk = wl.work()
-    g_s = (gu_ms + dn_ms) * 1e-3
+    g_s = ffn_ms * 1e-3  # the grouped gate/up + down call the layer uses
     out = dict(
         tokens_per_s=1.0 / (step_ms * 1e-3), ms_per_step=step_ms, timing="hip graph replay",
         eager_tokens_per_s=200 / w_eager,
-        route_ms=round(route_ms, 5), gate_up_ms=round(gu_ms, 5), down_ms=round(dn_ms, 5),
-        combine_ms=round(cb_ms, 5),
+        route_ms=round(route_ms, 5), ffn_ms=round(ffn_ms, 5), combine_ms=round(cb_ms, 5),
+        gate_up_ms=round(gu_ms, 5), down_ms=round(dn_ms, 5),
         gate_up_hbm_gbs=wk["bytes_gate_up"] / (gu_ms * 1e-3) / 1e9,
         down_hbm_gbs=wk["bytes_down"] / (dn_ms * 1e-3) / 1e9,
         gemm_hbm_gbs=(wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9,

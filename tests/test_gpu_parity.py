@@ -262,6 +262,39 @@ def test_chunked16384_chunks(full_banks, chunk):
                 label=f"chunk {chunk}")
 
 
+@pytest.mark.parametrize("T", [1, 5, 16, 48])
+def test_grouped_ffn_matches_separate_calls(full_banks, T):
+    """moe_grouped_w4_ffn (the layer's path) against moe_w4_gate_up followed
+    by moe_w4_down: h and y_slots equal bit for bit, on several calls in a
+    row and after a fresh route, with the status word clear."""
+    note(f"case grouped FFN T={T}")
+    c = build_config("decode1", T=T, t0=500, with_weights=False)
+    sh = c["shape"]
+    routed_np, shared_np, routed_dev, shared_dev = full_banks
+    layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, routed_dev, shared_dev, c["wr"],
+                         c["bias"], T_max=T, tile_m_max=32)
+    x = dev(c["x"])
+    d = layer.route(x)
+    layer.gate_up(d, x)
+    layer.down(d)
+    torch.cuda.synchronize()
+    h_ref, ys_ref = layer.h.clone(), layer.y_slots.clone()
+    for rep in range(3):
+        layer.h.zero_()
+        layer.y_slots.zero_()
+        layer.ffn(d, x)
+        torch.cuda.synchronize()
+        assert int(layer.rt.status.item()) == 0, rep
+        assert torch.equal(layer.h, h_ref), rep
+        assert torch.equal(layer.y_slots, ys_ref), rep
+    # a fresh route call between fused calls also leaves everything consistent
+    d = layer.route(x)
+    layer.ffn(d, x)
+    torch.cuda.synchronize()
+    assert int(layer.rt.status.item()) == 0
+    assert torch.equal(layer.y_slots, ys_ref)
+
+
 @pytest.mark.parametrize("tok", [0, 1, 999])
 def test_decode1_tokens(full_banks, tok):
     check_layer("decode1", T=1, t0=tok, banks=full_banks, label=f"decode token {tok}")

@@ -318,12 +318,18 @@ class MoeLayer:
         s = shared or self.shared
         moe_w4_down(d, self.rt.c, r.c, s.c if s is not None else None, self.h, self.y_slots, stream)
 
+    def ffn(self, d, x, routed=None, shared=None, stream=None):
+        """gate/up then down through the library's grouped call."""
+        r = routed or self.routed
+        s = shared or self.shared
+        moe_grouped_w4_ffn(d, x, self.rt.c, r.c, s.c if s is not None else None, self.h,
+                           self.y_slots, stream)
+
     def combine(self, d, y, stream=None):
         moe_combine(d, self.rt.c, self.y_slots, y, stream)
 
     def forward(self, x, y, routed=None, shared=None, stream=None):
         d = self.route(x, stream=stream)
-        self.gate_up(d, x, routed, shared, stream)
-        self.down(d, routed, shared, stream)
+        self.ffn(d, x, routed, shared, stream)
         self.combine(d, y, stream)
         return y
