@@ -42,6 +42,10 @@ constexpr int kSmallM = 32;       // tiles up to this height go to the small-til
 // workgroups per CU at the kernel's register budget, the same sixteen waves
 // as two eight-wave workgroups but with finer-grained scheduling.
 constexpr int kSmallWaves = 4;
+// 16-row weight slices per small-tile wave.  One slice a wave halves the
+// registers (five or six waves per SIMD) but doubles the activation-fragment
+// reads per slice and was slower (gate/up 92 against 79 us at 512 tokens).
+constexpr int kSmallSlices = 2;
 
 // Raw operands of one step for one 16-row slice: the lane's four code words
 // (word j for MFMA j) and the (scale, bias) dwords of its row for the step's
@@ -206,7 +210,7 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 // (one per lane of a group) so that every lane stores unconditionally.
 constexpr int kXsWords = 2 * 2 * 8 * kSmallM;
 
-template <int WAVES, bool GATE_UP>
+template <int WAVES, int SW, bool GATE_UP>
 __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
@@ -222,11 +226,11 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   const int mtiles = bi.tm >> 4;
   const int row0 = bi.row0, rows = bi.rows;
 
-  bool sl_on[2];
-  const uint8_t* sbase[2];  // slice's first block
+  bool sl_on[SW];
+  const uint8_t* sbase[SW];  // slice's first block
 #pragma unroll
-  for (int sl = 0; sl < 2; ++sl) {
-    const int c = bi.nt * (2 * WAVES) + wave * 2 + sl;
+  for (int sl = 0; sl < SW; ++sl) {
+    const int c = bi.nt * (SW * WAVES) + wave * SW + sl;
     sl_on[sl] = c < nslices;
     sbase[sl] = bi.P + static_cast<size_t>(sl_on[sl] ? c : 0) * nk * kPackBlock;
   }
@@ -270,29 +274,29 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     }
   };
   // steps past the end reload the last step (never used): no branch
-  auto load_codes = [&](int s, SliceOps (&o)[2]) {
+  auto load_codes = [&](int s, SliceOps (&o)[SW]) {
     const size_t off = static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) load_slice(sbase[sl] + off, lane, o[sl]);
+    for (int sl = 0; sl < SW; ++sl) load_slice(sbase[sl] + off, lane, o[sl]);
   };
 
-  f32x4 acc[2][2];
+  f32x4 acc[2][SW];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < SW; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Per step: operands 128 + q of both slices and their groups' affine
   // terms; per 16-row tile and group, X = sum a over the group (staged with
   // the activations), then P per slice and the scale-after update.
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const PairConsts pk = pair_consts();
-  auto step = [&](int s, SliceOps (&o)[2], int buf, AChunks& ar) {
+  auto step = [&](int s, SliceOps (&o)[SW], int buf, AChunks& ar) {
     // this step's codes leave the prefetch registers before the next load
-    uint32_t qw[2][4];
-    float gs[2][2], gc[2][2];
+    uint32_t qw[SW][4];
+    float gs[SW][2], gc[SW][2];
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
+    for (int sl = 0; sl < SW; ++sl) {
       qw[sl][0] = o[sl].q.x;
       qw[sl][1] = o[sl].q.y;
       qw[sl][2] = o[sl].q.z;
@@ -304,9 +308,9 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     if (active) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        bf16x8 bq[2][2];
+        bf16x8 bq[SW][2];
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
+        for (int sl = 0; sl < SW; ++sl) {
           bq[sl][0] = codes_plus128(qw[sl][2 * g], pk);
           bq[sl][1] = codes_plus128(qw[sl][2 * g + 1], pk);
         }
@@ -319,7 +323,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
             const f32x4 X = *reinterpret_cast<const f32x4*>(
                 &Xs[((buf * 2 + g) * 8) * kSmallM + mt * 16 + 4 * (lane >> 4)]);
 #pragma unroll
-            for (int sl = 0; sl < 2; ++sl) {
+            for (int sl = 0; sl < SW; ++sl) {
               f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
               P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq[sl][1], P, 0, 0, 0);
 #pragma unroll
@@ -335,7 +339,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     __syncthreads();
   };
 
-  SliceOps c0[2], c1[2];
+  SliceOps c0[SW], c1[SW];
   load_codes(0, c0);
   load_codes(1, c1);
   AChunks ar;
@@ -357,8 +361,8 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
       const int m = mt * 16 + (lane >> 4) * 4 + i;
       const size_t r = static_cast<size_t>(row0 + m);
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const int c = bi.nt * (2 * WAVES) + wave * 2 + sl;
+      for (int sl = 0; sl < SW; ++sl) {
+        const int c = bi.nt * (SW * WAVES) + wave * SW + sl;
         const float v = acc[mt][sl][i];
         if (GATE_UP) {
           const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
@@ -374,7 +378,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   }
 }
 
-template <int WAVES, bool GATE_UP>
+template <int WAVES, int SW, bool GATE_UP>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
     GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
@@ -382,14 +386,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ int s_tok[kSmallM];
 
   BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi, 2 * WAVES)) return;
+  if (!block_info<GATE_UP>(a, bi, SW * WAVES)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
   if (GATE_UP) {
     block_tokens(a, bi, s_tok);
     __syncthreads();
   }
-  small_block<WAVES, GATE_UP>(a, bi, src, out, As, Xs, s_tok);
+  small_block<WAVES, SW, GATE_UP>(a, bi, src, out, As, Xs, s_tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -857,9 +861,9 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
                               hipStream_t stream) {
   if (a.T <= kGemvRows) return launch_gemv<GATE_UP>(a, src, out, stream);
   const long long blocks8 = (a.max_blocks + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kSmallWaves)));
-  hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, GATE_UP>), grid_small, dim3(64 * kSmallWaves), 0,
-                     stream, a, src, out);
+  const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves)));
+  hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP>), grid_small,
+                     dim3(64 * kSmallWaves), 0, stream, a, src, out);
   if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kTallWaves)));
     hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, a, src, out);
