@@ -336,23 +336,26 @@ def test_routing_batch_sizes(full_banks, T):
 
 # ----------------------------------------------------------------------------- odd shapes
 
-@pytest.mark.parametrize("H,I,E,k,n_shared,T", [
-    (192, 64, 5, 5, 1, 33),     # K tails (H % 128 = 64, I = 64), E < 32, k = E
-    (128, 128, 40, 1, 0, 70),   # no shared expert, k = 1
-    (256, 192, 33, 3, 1, 9),    # E not a multiple of 32, I % 128 = 64
-    (1088, 320, 24, 4, 1, 5),   # short batch: inputs split over two waves, K tails in both GEMMs
-    (2112, 64, 16, 2, 1, 3),    # short batch: a wave with more steps than one load chunk
+@pytest.mark.parametrize("H,I,E,k,n_shared,T,tile_m_max", [
+    (192, 64, 5, 5, 1, 33, 32),     # K tails (H % 128 = 64, I = 64), E < 32, k = E
+    (128, 128, 40, 1, 0, 70, 32),   # no shared expert, k = 1
+    (256, 192, 33, 3, 1, 9, 32),    # E not a multiple of 32, I % 128 = 64
+    (1088, 320, 24, 4, 1, 5, 32),   # short batch: inputs split over two waves, K tails in both GEMMs
+    (2112, 64, 16, 2, 1, 3, 32),    # short batch: a wave with more steps than one load chunk
+    (192, 64, 5, 5, 1, 200, 128),   # tall tiles (every expert 200 rows: blocks of 100) with K tails
+    (1088, 320, 24, 4, 1, 300, 128),  # tall and small tiles, K tails in both GEMMs
 ])
-def test_odd_shapes(H, I, E, k, n_shared, T):
-    note(f"case odd shape H={H} I={I} E={E} k={k} shared={n_shared} T={T}")
+def test_odd_shapes(H, I, E, k, n_shared, T, tile_m_max):
+    note(f"case odd shape H={H} I={I} E={E} k={k} shared={n_shared} T={T} tile {tile_m_max}")
     routed = make_bank(E, H, I, seed=21, prefix="odd")
     shared = make_bank(1, H, I, seed=21, prefix="odd_shared") if n_shared else None
     wr = make_router(H, E, 0.1, seed=21)
     x = make_tokens(T, H, seed=21)
     rd = moe.DeviceBank(routed)
     sd = moe.DeviceBank(shared) if n_shared else None
-    _, g, y = run_layer(x, wr, None, routed, shared, rd, sd, k, tile_m_max=32, n_shared=n_shared)
-    r = oracle.route(x, wr, None, k, n_shared, 32, 16, NTHREADS)
+    _, g, y = run_layer(x, wr, None, routed, shared, rd, sd, k, tile_m_max=tile_m_max,
+                        n_shared=n_shared)
+    r = oracle.route(x, wr, None, k, n_shared, tile_m_max, 16, NTHREADS)
     check_routing(g, r)
     yref = oracle.moe_layer(x, r["topk_idx"], r["topk_w"], routed, shared, nthreads=NTHREADS)
     assert oracle.relative_error(y_to_f64(y), yref) <= TOL_Y
