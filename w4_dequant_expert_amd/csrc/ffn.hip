@@ -140,7 +140,8 @@ struct BlockInfo {
 };
 
 // Workgroups are dealt to the eight XCDs round-robin (workgroup i runs on
-// XCD i mod 8).  Blocks are dealt the same way -- block b to XCD b mod 8 --
+// XCD i mod 8).  Blocks (in the order below) are dealt the same way -- block
+// b to XCD b mod 8 --
 // with all N tiles of a block, which read the same activation rows, on the
 // block's XCD so that they share its L2: workgroup i takes block
 // 8 * ((i / 8) / ntiles) + i mod 8 and N tile (i / 8) mod ntiles.  The grid
@@ -162,7 +163,11 @@ __device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi, int
   bi.nt = r % ntiles;
   const int nblk = min(*a.n_blocks, a.max_blocks);
   if (bid >= nblk) return false;
-  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
+  // The shared expert's blocks, last in the map, are dealt first: they all
+  // stream the same weights, and started together with the routed blocks
+  // they no longer form the last, partly filled round of workgroups alone.
+  const int nsh = min(a.n_shared_blocks, nblk);
+  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[(bid + nblk - nsh) % nblk];
   bi.G = blk.x;
   bi.row0 = blk.y;
   bi.rows = blk.z;

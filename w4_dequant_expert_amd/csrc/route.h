@@ -34,6 +34,7 @@ struct GemmArgs {
   const int32_t* sorted_slot;
   BankView routed, shared;
   uint32_t* status;
+  int n_shared_blocks;  // blocks of the shared expert (the last ones of the map)
 };
 
 // M_MAX: largest tile height the chosen kernel variant accepts (64, 128, 256).
