@@ -207,9 +207,9 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 }
 
 // ---------------------------------------------------------------------------
-// Small-tile kernel: blocks of at most 32 rows.  WAVES waves, two slices
-// each (a workgroup covers 2 WAVES slices of one block); each thread stages
-// 32 * 16 / (64 WAVES) activation chunks per step.
+// Small-tile kernel: blocks of at most 32 rows.  WAVES waves, SW slices
+// each (a workgroup covers SW * WAVES slices of one block); each thread
+// stages 32 * 16 / (64 WAVES) activation chunks per step.
 // ---------------------------------------------------------------------------
 // Group sums of the staged activations: Xs[buf][g][copy][row], eight copies
 // (one per lane of a group) so that every lane stores unconditionally.
