@@ -59,7 +59,7 @@ def lib():
         import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it first "
-                              "(python -m w4_dequant_expert_amd.build)")
+                              "(python __graft_entry__.py, or python w4_dequant_expert_amd/build.py)")
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         vp = ctypes.c_void_p
