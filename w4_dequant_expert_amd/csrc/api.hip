@@ -46,7 +46,7 @@ int validate_dims(const moe_dims* d) {
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-  size_t logits, bits, pref, total;
+  size_t logits, bits, pref, part, total;
 };
 
 WsLayout ws_layout(const moe_dims& d, bool need_logits) {
@@ -60,6 +60,8 @@ WsLayout ws_layout(const moe_dims& d, bool need_logits) {
   off += align256(W * E * 4);
   L.pref = off;
   off += align256(W * E * 4);
+  L.part = off;  // router class sums of the short-batch path
+  off += (T <= 16 && E <= 256) ? align256(8 * T * E * 4) : 0;
   L.total = off;
   return L;
 }
@@ -189,6 +191,7 @@ int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const
   rb.n_blocks = out->n_blocks;
   rb.bits = reinterpret_cast<uint32_t*>(ws + L.bits);
   rb.pref = reinterpret_cast<int32_t*>(ws + L.pref);
+  rb.part = reinterpret_cast<float*>(ws + L.part);
   rb.status = out->status;
   rb.max_blocks = max_blocks_of(*d);
   (void)hipGetLastError();

@@ -20,6 +20,7 @@ struct RouteBuffers {
   int32_t* n_blocks;     // [1]
   uint32_t* bits;        // [ceil(T/32)][E] token bitmask per expert   (workspace)
   int32_t* pref;         // [ceil(T/32)][E] tokens before each word     (workspace)
+  float* part;           // [8][T][E] router class sums, T <= 16 and E <= 256 (workspace)
   uint32_t* status;
   int max_blocks;
 };

@@ -271,6 +271,103 @@ __global__ __launch_bounds__(1024) void router_scores_short_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// K1 for short batches with E <= 256, spread over eight times as many
+// workgroups.  The tree's first three levels (s = 32, 16, 8) only ever add
+// partials whose indices agree mod 8, so the 64 partials of an output split
+// into eight classes m = q (mod 8) that reduce independently: workgroup
+// (expert chunk, q) runs the chains of the eight partials of class q for 16
+// experts and every token, reduces them with those three levels in LDS, and
+// writes the class sum to part[q][t][e].  The last three levels (s = 4, 2, 1)
+// over the eight class sums and the bias are applied by route_short_kernel,
+// so the evaluation order is exactly that of the full tree.  Only the inputs
+// h = q (mod 8) are staged, as float32.
+// ---------------------------------------------------------------------------
+constexpr int kClasses = 8;
+
+template <int TT>  // batch bucket: T <= TT; rows T..TT-1 are computed and dropped
+__global__ __launch_bounds__(128) void router_partials_short_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wr,
+    float* __restrict__ part, uint32_t* __restrict__ status) {
+  __shared__ float xs[TT][kShortHC / kClasses];
+  __shared__ float ps[TT][kClasses][17];
+
+  const int tid = threadIdx.x;
+  const int q = blockIdx.x % kClasses;
+  const int es = tid & 15, mi = tid >> 4;  // partial m = q + 8 mi
+  const int m = q + kClasses * mi;
+  const int e = (blockIdx.x / kClasses) * 16 + es, ec = min(e, E - 1);
+  if (blockIdx.x == 0 && tid == 0) *status = 0u;
+
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+
+  for (int c = 0; c < H; c += kShortHC) {
+    const int ni = min(kShortHC, H - c) / 64;  // chain steps of this pass
+    float wv[kShortIU];
+#pragma unroll
+    for (int i = 0; i < kShortIU; ++i)
+      wv[i] = wr[static_cast<size_t>(c + min(i, ni - 1) * 64 + m) * E + ec];
+    // x[t][c + 8 j + q], j < 8 ni: XU values per thread, all loads in flight together
+    constexpr int XU = TT * (kShortHC / kClasses) / 128;
+    const int nv = T * ni * 8;
+    uint16_t xv[XU];
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int v = min(tid + u * 128, nv - 1);
+      const int t = v / (ni * 8), j = v % (ni * 8);
+      xv[u] = x[static_cast<size_t>(t) * H + c + 8 * j + q];
+    }
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int v = tid + u * 128;
+      if (v < nv) xs[v / (ni * 8)][v % (ni * 8)] = bf16_to_f32(xv[u]);
+    }
+    __syncthreads();
+    // chain step i of partial m reads input c + 64 i + m = c + 8 (8 i + mi) + q
+#pragma unroll
+    for (int i = 0; i < kShortIU; ++i) {
+      if (i < ni) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[t] = __builtin_fmaf(xs[t][8 * i + mi], wv[i], acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) ps[t][mi][es] = acc[t];
+  __syncthreads();
+  // levels s = 32, 16, 8 of the tree: partial m + s is index mi + s / 8
+#pragma unroll
+  for (int s2 = 4; s2 >= 1; s2 >>= 1) {
+    if (mi < s2) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) ps[t][mi][es] = ps[t][mi][es] + ps[t][mi + s2][es];
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < T * 16; i += 128) {
+    const int t = i >> 4, j = i & 15;
+    const int eo = (blockIdx.x / kClasses) * 16 + j;
+    if (eo < E) part[(static_cast<size_t>(q) * T + t) * E + eo] = ps[t][0][j];
+  }
+}
+
+// Score of (t, e) from its eight class sums: the tree's levels s = 4, 2, 1,
+// then the bias.
+__device__ __forceinline__ float score_from_classes(const float* __restrict__ part, int T, int E,
+                                                    int t, int e, const float* __restrict__ bias) {
+  float p[kClasses];
+#pragma unroll
+  for (int i = 0; i < kClasses; ++i) p[i] = part[(static_cast<size_t>(i) * T + t) * E + e];
+#pragma unroll
+  for (int s = kClasses / 2; s >= 1; s >>= 1)
+#pragma unroll
+    for (int i = 0; i < s; ++i) p[i] = p[i] + p[i + s];
+  return bias ? p[0] + bias[e] : p[0];
+}
+
+// ---------------------------------------------------------------------------
 // K2: top-k and weights.  A token is served by one 16-lane row of a wave
 // (four tokens per wave); lane r holds the scores of experts r, r+16, r+32...
 // Every score becomes a 64-bit key: an order-preserving image of the float32
@@ -694,7 +791,8 @@ __global__ __launch_bounds__(1024) void route_scan_lds_kernel(
 template <int VPL>
 __global__ __launch_bounds__(1024) void route_short_kernel(
     int T, int E, int k, int n_shared, int tile_m_max, int tile_gran,
-    const float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    const float* __restrict__ part, const float* __restrict__ bias,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ blocks, int32_t* __restrict__ n_blocks,
     int max_blocks, uint32_t* __restrict__ status) {
@@ -704,14 +802,21 @@ __global__ __launch_bounds__(1024) void route_short_kernel(
   __shared__ int s_bstart[kMaxE + 2];
   __shared__ int s_cnt[kMaxE + 1];
   __shared__ int tmp[17];
+  __shared__ float s_logit[kShortT * 16 * VPL];
   const int tid = threadIdx.x;
   const int S = T * k;
   for (int e = tid; e < E; e += 1024) s_bits[e] = 0u;
+  // scores from the class sums of router_partials_short_kernel (exported too)
+  for (int i = tid; i < T * E; i += 1024) {
+    const float l = score_from_classes(part, T, E, i / E, i % E, bias);
+    s_logit[i] = l;
+    logits[i] = l;
+  }
   __syncthreads();
   if (tid < kShortT * 16) {  // a full row of lanes per token slot, t < T or not
     const int t = tid >> 4, r = tid & 15;
     int sa, sb;
-    topk_row<VPL>(T, E, k, logits, t, topk_idx, topk_w, status, sa, sb);
+    topk_row<VPL>(T, E, k, s_logit, t, topk_idx, topk_w, status, sa, sb);
     if (sa >= 0) {
       s_sel[t * k + r] = sa;
       atomicOr(&s_bits[sa], 1u << t);
@@ -741,7 +846,24 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
   const int nbits = ((T + 31) / 32) * E;
   // 16-byte router loads only when every row start is 16-byte aligned
   const int vec_wr = (E % 4 == 0) && (reinterpret_cast<uintptr_t>(wr) % 16 == 0);
-  if (T <= kShortT) {  // decode-sized batches: spread over the router matrix
+  if (T <= kShortT && E <= 256) {  // decode-sized batches: class sums, then one workgroup
+    const dim3 g((E + 15) / 16 * kClasses);
+#define MOE_PART(TT)                                                                              \
+  hipLaunchKernelGGL(router_partials_short_kernel<TT>, g, dim3(128), 0, stream, T, d.H, E, x, wr, \
+                     rb.part, rb.status)
+    if (T <= 1) MOE_PART(1);
+    else if (T <= 2) MOE_PART(2);
+    else if (T <= 4) MOE_PART(4);
+    else if (T <= 8) MOE_PART(8);
+    else MOE_PART(16);
+#undef MOE_PART
+    hipLaunchKernelGGL((route_short_kernel<16>), dim3(1), dim3(1024), 0, stream, T, E, k,
+                       d.n_shared, d.tile_m_max, d.tile_gran, rb.part, bias, rb.logits,
+                       rb.topk_idx, rb.topk_w, rb.counts, rb.offsets, rb.sorted_slot, rb.slot_pos,
+                       rb.blocks, rb.n_blocks, rb.max_blocks, rb.status);
+    return hipGetLastError();
+  }
+  if (T <= kShortT) {  // decode-sized batches with more experts: spread over the router matrix
     const dim3 g((E + 15) / 16);
 #define MOE_SHORT(TT)                                                                      \
   hipLaunchKernelGGL(router_scores_short_kernel<TT>, g, dim3(1024), 0, stream, T, d.H, E, x, wr, \
@@ -768,13 +890,6 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
     else
       hipLaunchKernelGGL((router_scores_kernel<2, 2, 4, false>), g1, dim3(256), 0, stream, T,
                          d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
-  }
-  if (T <= kShortT && E <= 256) {  // top-k, tables and scatter in one workgroup
-    hipLaunchKernelGGL((route_short_kernel<16>), dim3(1), dim3(1024), 0, stream, T, E, k,
-                       d.n_shared, d.tile_m_max, d.tile_gran, rb.logits, rb.topk_idx, rb.topk_w,
-                       rb.counts, rb.offsets, rb.sorted_slot, rb.slot_pos, rb.blocks, rb.n_blocks,
-                       rb.max_blocks, rb.status);
-    return hipGetLastError();
   }
   const dim3 g2((T + 15) / 16);
   if (E <= 256)
