@@ -133,6 +133,7 @@ GemmArgs gemm_args(const moe_dims& d, const moe_route_out* r, const moe_w4_bank*
   a.shared = view(d.n_shared ? shared : nullptr);
   a.status = r->status;
   a.n_shared_blocks = d.n_shared ? (d.T + d.tile_m_max - 1) / d.tile_m_max : 0;
+  a.tile_gran = d.tile_gran;
   return a;
 }
 

@@ -161,13 +161,26 @@ __device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi, int
   const int r = blockIdx.x / kXcds;
   const int bid = kXcds * (r / ntiles) + blockIdx.x % kXcds;
   bi.nt = r % ntiles;
-  const int nblk = min(*a.n_blocks, a.max_blocks);
-  if (bid >= nblk) return false;
   // The shared expert's blocks, last in the map, are dealt first: they all
   // stream the same weights, and started together with the routed blocks
   // they no longer form the last, partly filled round of workgroups alone.
-  const int nsh = min(a.n_shared_blocks, nblk);
-  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[(bid + nblk - nsh) % nblk];
+  // Their entries follow from T and the tile bounds (the shared group always
+  // holds T rows), so those workgroups load nothing to find their block.
+  const int nsh = a.n_shared_blocks;
+  if (bid < nsh) {
+    const int bs = a.T / nsh, rem = a.T % nsh;
+    bi.G = a.E;
+    bi.row0 = a.T * a.k + bid * bs + min(bid, rem);
+    bi.rows = bs + (bid < rem ? 1 : 0);
+    bi.tm = (bs + (rem > 0 ? 1 : 0) + a.tile_gran - 1) / a.tile_gran * a.tile_gran;
+    return true;
+  }
+  // A routed block: its entry is loaded together with the map length (the
+  // index is in bounds either way), not after it.
+  const int rb = bid - nsh;
+  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[min(rb, a.max_blocks - 1)];
+  const int nblk = min(*a.n_blocks, a.max_blocks);
+  if (rb >= nblk - nsh) return false;
   bi.G = blk.x;
   bi.row0 = blk.y;
   bi.rows = blk.z;
@@ -220,7 +233,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
                                             uint16_t (*As)[kSmallM * kLDA], float* Xs,
-                                            const int* s_tok) {
+                                            int* s_tok) {
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int nk = pack_steps(K);
@@ -240,6 +253,22 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     sbase[sl] = bi.P + static_cast<size_t>(sl_on[sl] ? c : 0) * nk * kPackBlock;
   }
   const bool active = sl_on[0];
+
+  // steps past the end reload the last step (never used): no branch
+  auto load_codes = [&](int s, SliceOps (&o)[SW]) {
+    const size_t off = static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
+#pragma unroll
+    for (int sl = 0; sl < SW; ++sl) load_slice(sbase[sl] + off, lane, o[sl]);
+  };
+  // The codes of steps 0 and 1 do not depend on the block's tokens: they are
+  // in flight while the token list is gathered.
+  SliceOps c0[SW], c1[SW];
+  load_codes(0, c0);
+  load_codes(1, c1);
+  if (GATE_UP) {
+    block_tokens(a, bi, s_tok);
+    __syncthreads();
+  }
 
   // A staging: tm rows x 16 chunks of 16 bytes, NPASS chunks per thread
   // (rows am, am + 4 WAVES, ...); rows past the block read row 0 and are zeroed
@@ -278,13 +307,6 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
       Xs[((buf * 2 + (ac >> 3)) * 8 + (ac & 7)) * kSmallM + am[p]] = sum_lanes8(sum8_bf16(v));
     }
   };
-  // steps past the end reload the last step (never used): no branch
-  auto load_codes = [&](int s, SliceOps (&o)[SW]) {
-    const size_t off = static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
-#pragma unroll
-    for (int sl = 0; sl < SW; ++sl) load_slice(sbase[sl] + off, lane, o[sl]);
-  };
-
   f32x4 acc[2][SW];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -344,9 +366,6 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     __syncthreads();
   };
 
-  SliceOps c0[SW], c1[SW];
-  load_codes(0, c0);
-  load_codes(1, c1);
   AChunks ar;
   load_a(0, ar);
   store_a(0, ar, 0);
@@ -394,10 +413,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
   if (!block_info<GATE_UP>(a, bi, SW * WAVES)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
-  if (GATE_UP) {
-    block_tokens(a, bi, s_tok);
-    __syncthreads();
-  }
   small_block<WAVES, SW, GATE_UP>(a, bi, src, out, As, Xs, s_tok);
 }
 
@@ -467,7 +482,7 @@ __device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& b
                                            const uint16_t* __restrict__ src,
                                            uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
                                            uint8_t* As2, uint8_t* Cs0, uint8_t* Cs1, uint8_t* Cs2,
-                                           const int* s_tok) {
+                                           int* s_tok) {
   constexpr int NCP = MT;  // activation copies per wave per step (4 rows each)
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
@@ -487,13 +502,7 @@ __device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& b
   // into LDS bytes [1024 q, 1024 q + 1024); lane -> row 4q + lane/16, stored
   // chunk lane % 16, which holds the row's chunk cg = (lane % 16) ^ (row % 16).
   const int cg = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
-  const uint16_t* arow[NCP];
-#pragma unroll
-  for (int i = 0; i < NCP; ++i) {
-    const int r = min(4 * (kTallWaves * i + wave) + (lane >> 4), rows - 1);
-    const int srow = GATE_UP ? max(s_tok[r], 0) : row0 + r;
-    arow[i] = src + static_cast<size_t>(srow) * K;
-  }
+  const uint16_t* arow[NCP];  // set once the block's tokens are known
   auto issue_a = [&](int s, uint8_t* buf) {
     const int kk = min(min(s, nk - 1) * kKS + cg * 8, K - 8);
 #pragma unroll
@@ -621,11 +630,26 @@ __device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& b
     }
   };
 
-  issue_a(0, As0);
+  // The codes of steps 0 and 1 do not depend on the block's tokens: they are
+  // in flight while the token list is gathered.  Then the activations of
+  // steps 0 and 1; waiting for all but the last NCP copies leaves only the
+  // activations of step 1 in flight, which re-establishes the loop's
+  // invariant (the copies of step s have landed at its start).
   issue_codes(0, Cs0);
-  issue_a(1, As1);
   issue_codes(1, Cs1);
-  wait_vmcnt<kInFlight>();  // activations and codes of step 0
+  if (GATE_UP) {
+    block_tokens(a, bi, s_tok);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int r = min(4 * (kTallWaves * i + wave) + (lane >> 4), rows - 1);
+    const int srow = GATE_UP ? max(s_tok[r], 0) : row0 + r;
+    arow[i] = src + static_cast<size_t>(srow) * K;
+  }
+  issue_a(0, As0);
+  issue_a(1, As1);
+  wait_vmcnt<NCP>();  // codes of steps 0 and 1, activations of step 0
   read_codes(Cs0, tc);
   bq[0] = rebuild_j(tc, 0);
   int s = 0;
@@ -676,10 +700,6 @@ __global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
   if (!block_info<GATE_UP>(a, bi, 2 * kTallWaves)) return;
   if (bi.tm <= kSmallM) return;  // a short block: the small-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
-  if (GATE_UP) {
-    block_tokens(a, bi, s_tok);
-    __syncthreads();
-  }
   switch ((bi.tm + 31) >> 5) {
     case 2: tall_block<2, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
     case 3: tall_block<3, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
@@ -709,11 +729,13 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int ntiles = (nslices + SPW - 1) / SPW;
   const int bid = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+  // bid < max_blocks (grid size): the entry is loaded together with the map
+  // length, not after it
+  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
   const int nblk = min(*a.n_blocks, a.max_blocks);
   if (bid >= nblk) return;
   BlockInfo bi;
   {
-    const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
     bi.G = blk.x;
     bi.row0 = blk.y;
     bi.rows = blk.z;

@@ -36,6 +36,7 @@ struct GemmArgs {
   BankView routed, shared;
   uint32_t* status;
   int n_shared_blocks;  // blocks of the shared expert (the last ones of the map)
+  int tile_gran;        // tile heights are multiples of this
 };
 
 // M_MAX: largest tile height the chosen kernel variant accepts (64, 128, 256).
