@@ -417,9 +417,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ---------------------------------------------------------------------------
-// Tall-tile kernel: blocks of 48..128 rows, computed as MT = 2..4 row tiles of
-// 32 with v_mfma_f32_32x32x16_bf16 (on gfx950 the 32x32 form delivers twice
-// the 16x16 form's throughput).  Eight waves, two per SIMD: each owns two
+// Tall-tile kernel: blocks of 48..128 rows (and, for large batches, every
+// block), computed as MT = 1..4 row tiles of 32 with v_mfma_f32_32x32x16_bf16
+// (on gfx950 the 32x32 form delivers twice the 16x16 form's throughput).  Eight waves, two per SIMD: each owns two
 // weight slices (one 32-column tile) and all of the block's rows, so each
 // rebuilt weight feeds MT MFMAs, and the two waves of a SIMD overlap each
 // other's matrix, vector and LDS work (one wave per SIMD leaves the matrix
@@ -698,9 +698,10 @@ __global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
 
   BlockInfo bi;
   if (!block_info<GATE_UP>(a, bi, 2 * kTallWaves)) return;
-  if (bi.tm <= kSmallM) return;  // a short block: the small-tile kernel owns it
+  if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
   switch ((bi.tm + 31) >> 5) {
+    case 1: tall_block<1, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
     case 2: tall_block<2, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
     case 3: tall_block<3, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
     default: tall_block<4, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
@@ -888,12 +889,21 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
                               hipStream_t stream) {
   if (a.T <= kGemvRows) return launch_gemv<GATE_UP>(a, src, out, stream);
   const long long blocks8 = (a.max_blocks + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves)));
-  hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP>), grid_small,
-                     dim3(64 * kSmallWaves), 0, stream, a, src, out);
+  // When tall tiles are allowed and an expert averages at least kSmallM rows,
+  // nearly all rows sit in tall blocks; the few short blocks then run in the
+  // tall-tile kernel too (one 32-row tile), where they fill its last round of
+  // workgroups instead of occupying a launch of their own that the chip
+  // cannot fill.
+  GemmArgs ga = a;
+  ga.tall_all = m_max && static_cast<long long>(a.T) * a.k >= static_cast<long long>(kSmallM) * a.E;
+  if (!ga.tall_all) {
+    const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves)));
+    hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP>), grid_small,
+                       dim3(64 * kSmallWaves), 0, stream, ga, src, out);
+  }
   if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kTallWaves)));
-    hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, a, src, out);
+    hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, ga, src, out);
   }
   return hipGetLastError();
 }

@@ -37,6 +37,7 @@ struct GemmArgs {
   uint32_t* status;
   int n_shared_blocks;  // blocks of the shared expert (the last ones of the map)
   int tile_gran;        // tile heights are multiples of this
+  int tall_all;         // set by the launcher: the tall-tile kernel takes every block
 };
 
 // M_MAX: largest tile height the chosen kernel variant accepts (64, 128, 256).
