@@ -720,7 +720,9 @@ __global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
 constexpr int kGemvRows = 16;   // rows per block this kernel accepts
 constexpr int kGemvChunk = 4;   // steps whose loads are in flight together
 
-template <int KS, bool GATE_UP>
+// ONE: a single-token batch, where every gate/up row reads x row 0, so the
+// activation loads need not wait for the slot-to-token lookup.
+template <int KS, bool GATE_UP, bool ONE>
 __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t* __restrict__ src,
                                                       uint16_t* __restrict__ out) {
   constexpr int SPW = 4 / KS;  // slices per workgroup
@@ -763,7 +765,7 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   const int r = lane & 15;
   const int Sk = a.T * a.k;
   const int rr = bi.row0 + min(r, bi.rows - 1);
-  int srow = GATE_UP ? ((rr < Sk) ? a.sorted_slot[rr] : rr) : rr;
+  int srow = (GATE_UP && !ONE) ? ((rr < Sk) ? a.sorted_slot[rr] : rr) : rr;
 
   auto load_w = [&](int s0, SliceOps (&o)[kGemvChunk]) {
 #pragma unroll
@@ -773,7 +775,9 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   SliceOps o0[kGemvChunk];
   load_w(s_begin, o0);
 
-  if (GATE_UP) {
+  if (GATE_UP && ONE) {
+    srow = 0;
+  } else if (GATE_UP) {
     srow = (rr < Sk) ? srow / a.k : rr - Sk;
     if (srow < 0 || srow >= a.T) {
       status_set(a.status, MOE_STATUS_BAD_INDEX);
@@ -872,12 +876,17 @@ static hipError_t launch_gemv(const GemmArgs& a, const uint16_t* src, uint16_t* 
   const int ks = nk >= 16 ? 4 : nk >= 8 ? 2 : 1;
   const int spw = 4 / ks;
   const dim3 grid(static_cast<unsigned>(a.max_blocks) * ((nslices + spw - 1) / spw));
-  if (ks == 4)
-    hipLaunchKernelGGL((w4_gemv_kernel<4, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
-  else if (ks == 2)
-    hipLaunchKernelGGL((w4_gemv_kernel<2, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
-  else
-    hipLaunchKernelGGL((w4_gemv_kernel<1, GATE_UP>), grid, dim3(256), 0, stream, a, src, out);
+#define MOE_GEMV(KS, ONE) \
+  hipLaunchKernelGGL((w4_gemv_kernel<KS, GATE_UP, ONE>), grid, dim3(256), 0, stream, a, src, out)
+  const bool one = GATE_UP && a.T == 1;
+  if (ks == 4) {
+    if (one) MOE_GEMV(4, true); else MOE_GEMV(4, false);
+  } else if (ks == 2) {
+    if (one) MOE_GEMV(2, true); else MOE_GEMV(2, false);
+  } else {
+    if (one) MOE_GEMV(1, true); else MOE_GEMV(1, false);
+  }
+#undef MOE_GEMV
   return hipGetLastError();
 }
 

@@ -589,6 +589,63 @@ __device__ void finish_tables(int T, int E, int k, int n_shared, int tile_m_max,
 
 }
 
+// Tables for batches of at most 16 tokens (E <= 256), in one wave and with no
+// workgroup barrier.  A group then holds at most 16 rows, never more than one
+// tile (tile_m_max >= 16), so each non-empty expert has exactly one block and
+// the shared group one.  Lane l owns experts 4l .. 4l+3; a single wave scan of
+// (block count << 16 | row count) gives every expert's offset and block index
+// (row counts total at most 16 * kMaxK, so the low half never carries).
+__device__ void short_tables_wave(int T, int E, int k, int n_shared, int tile_gran,
+                                  const uint32_t* s_bits, int* s_off,
+                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                  int32_t* __restrict__ blocks, int32_t* __restrict__ n_blocks,
+                                  int max_blocks, uint32_t* __restrict__ status) {
+  const int lane = threadIdx.x & 63;
+  const int S = T * k;
+  int c[4];
+  int packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    c[i] = (e < E) ? __popc(s_bits[e]) : 0;
+    packed += (c[i] > 0 ? (1 << 16) : 0) + c[i];
+  }
+  int inc = packed;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  const int tot = __shfl(inc, 63, 64);
+  const int total = tot & 0xFFFF, nb_routed = tot >> 16;
+  int run = inc - packed;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    const int off = run & 0xFFFF, b = run >> 16;
+    if (e < E) {
+      counts[e] = c[i];
+      offsets[e] = off;
+      s_off[e] = off;
+    }
+    if (c[i] > 0 && b < max_blocks)
+      reinterpret_cast<int4*>(blocks)[b] =
+          make_int4(e, off, c[i], (c[i] + tile_gran - 1) / tile_gran * tile_gran);
+    run += (c[i] > 0 ? (1 << 16) : 0) + c[i];
+  }
+  if (lane == 0) {
+    const int nb_total = nb_routed + (n_shared ? 1 : 0);
+    offsets[E] = total;
+    s_off[E] = S;
+    if (total != S) status_set(status, MOE_STATUS_BAD_INDEX);
+    if (nb_total > max_blocks) status_set(status, MOE_STATUS_BLOCK_OVERFLOW);
+    *n_blocks = min(nb_total, max_blocks);
+    if (n_shared && nb_routed < max_blocks)
+      reinterpret_cast<int4*>(blocks)[nb_routed] =
+          make_int4(E, S, T, (T + tile_gran - 1) / tile_gran * tile_gran);
+  }
+}
+
 constexpr int kScatterU = 16;  // slots per thread per scatter pass
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(
@@ -798,10 +855,7 @@ __global__ __launch_bounds__(1024) void route_short_kernel(
     int max_blocks, uint32_t* __restrict__ status) {
   __shared__ uint32_t s_bits[kMaxE];         // bit t: token t selected expert e
   __shared__ int s_sel[kShortT * kMaxK];     // expert of slot t*k + j
-  __shared__ int s_off[kMaxE + 1];
-  __shared__ int s_bstart[kMaxE + 2];
-  __shared__ int s_cnt[kMaxE + 1];
-  __shared__ int tmp[17];
+  __shared__ int s_off[16 * VPL + 1];
   __shared__ float s_logit[kShortT * 16 * VPL];
   const int tid = threadIdx.x;
   const int S = T * k;
@@ -827,9 +881,10 @@ __global__ __launch_bounds__(1024) void route_short_kernel(
     }
   }
   __syncthreads();
-  const int cnt = (tid < E) ? __popc(s_bits[tid]) : 0;
-  finish_tables(T, E, k, n_shared, tile_m_max, tile_gran, cnt, s_cnt, s_off, s_bstart, tmp, counts,
-                offsets, blocks, n_blocks, max_blocks, status);
+  if (tid < 64)
+    short_tables_wave(T, E, k, n_shared, tile_gran, s_bits, s_off, counts, offsets, blocks,
+                      n_blocks, max_blocks, status);
+  __syncthreads();
   // stable scatter: row = expert offset + tokens before t that chose e
   for (int sl = tid; sl < S; sl += 1024) {
     const int t = sl / k, e = s_sel[sl];
