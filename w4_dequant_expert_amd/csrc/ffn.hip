@@ -224,15 +224,12 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 // each (a workgroup covers SW * WAVES slices of one block); each thread
 // stages 32 * 16 / (64 WAVES) activation chunks per step.
 // ---------------------------------------------------------------------------
-// Group sums of the staged activations: Xs[buf][g][copy][row], eight copies
-// (one per lane of a group) so that every lane stores unconditionally.
-constexpr int kXsWords = 2 * 2 * 8 * kSmallM;
 
 template <int WAVES, int SW, bool GATE_UP>
 __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
-                                            uint16_t (*As)[kSmallM * kLDA], float* Xs,
+                                            uint16_t (*As)[kSmallM * kLDA],
                                             int* s_tok) {
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
@@ -303,8 +300,6 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
       // am < kSmallM always: unconditional, so no divergent branch disturbs
       // the wait counts of the code prefetch
       *reinterpret_cast<uint4*>(&As[buf][am[p] * kLDA + ac * 8]) = v;
-      // the row's sum over the chunk's input group (eight lanes hold a group)
-      Xs[((buf * 2 + (ac >> 3)) * 8 + (ac & 7)) * kSmallM + am[p]] = sum_lanes8(sum8_bf16(v));
     }
   };
   f32x4 acc[2][SW];
@@ -314,9 +309,10 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     for (int sl = 0; sl < SW; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Per step: operands 128 + q of both slices and their groups' affine
-  // terms; per 16-row tile and group, X = sum a over the group (staged with
-  // the activations), then P per slice and the scale-after update.
+  // terms; per 16-row tile and group, X = sum a over the group and P per
+  // slice, both on the matrix core, then the scale-after update.
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = bf16_ones();
   const PairConsts pk = pair_consts();
   auto step = [&](int s, SliceOps (&o)[SW], int buf, AChunks& ar) {
     // this step's codes leave the prefetch registers before the next load
@@ -347,8 +343,10 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
             const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk + 64 * g];
             const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
             const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 32);
-            const f32x4 X = *reinterpret_cast<const f32x4*>(
-                &Xs[((buf * 2 + g) * 8) * kSmallM + mt * 16 + 4 * (lane >> 4)]);
+            // the rows' group sums on the matrix core (a ones operand), in the
+            // accumulator layout of P
+            f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, zero, 0, 0, 0);
+            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, X, 0, 0, 0);
 #pragma unroll
             for (int sl = 0; sl < SW; ++sl) {
               f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
@@ -406,14 +404,13 @@ template <int WAVES, int SW, bool GATE_UP>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
     GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
-  __shared__ __attribute__((aligned(16))) float Xs[kXsWords];
   __shared__ int s_tok[kSmallM];
 
   BlockInfo bi;
   if (!block_info<GATE_UP>(a, bi, SW * WAVES)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
-  small_block<WAVES, SW, GATE_UP>(a, bi, src, out, As, Xs, s_tok);
+  small_block<WAVES, SW, GATE_UP>(a, bi, src, out, As, s_tok);
 }
 
 // ---------------------------------------------------------------------------
