@@ -101,32 +101,6 @@ __device__ __forceinline__ bf16x8 bf16_ones() {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Sum of the eight bfloat16 values of a 16-byte chunk, in float32.
-__device__ __forceinline__ float sum8_bf16(uint4 v) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-  float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), one, 0.0f, false);
-  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), one, d, false);
-  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), one, d, false);
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), one, d, false);
-}
-
-// Value of another lane through a DPP lane pattern (CTRL: quad_perm or row
-// mirror encoding).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each aligned group of eight lanes (lane xor 1, xor 2, then the
-// mirror inside the half row, which pairs the two quads).
-__device__ __forceinline__ float sum_lanes8(float v) {
-  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_f32<0x141>(v);  // row_half_mirror
-  return v;
-}
-
 // Scale s and the folded bias b - 128 s of a packed (scale, bias) dword.
 __device__ __forceinline__ void group_affine(uint32_t sb, float& s, float& c) {
   s = __uint_as_float(sb << 16);
