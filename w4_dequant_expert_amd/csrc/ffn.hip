@@ -680,6 +680,208 @@ __global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// Four-wave tall-tile kernel: the same tiles and MFMA layout as the
+// eight-wave kernel above, but a workgroup covers 8 slices (128 columns) with
+// four waves, keeps only two activation buffers in LDS (64 KB) and loads the
+// weight codes straight into registers, so two workgroups share a CU.  Each
+// SIMD then holds waves of two workgroups whose step barriers, prologues and
+// epilogues fall at different times, and one workgroup's waits are covered
+// by the other's work; the price is that a block's activation rows are
+// staged by twice as many workgroups.  Both kernels own the same blocks; the
+// host launches one of them.
+//   Step s issues the codes of step s+1 (registers), then the activations of
+//   step s+1 (LDS, the buffer step s-1 read, free after step s's barrier).
+//   Before the last k-chunk of step s, all but the last NCP loads done means
+//   the codes of step s+1 have landed; at the start of step s+1 everything is
+//   waited for.
+// ---------------------------------------------------------------------------
+constexpr int kT4Waves = 4;
+constexpr int kT4Threads = kT4Waves * kWave;
+
+struct RawCodes {
+  uint4 ce, co;
+  uint2 g;
+};
+
+template <int MT, bool GATE_UP>
+__device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& bi,
+                                            const uint16_t* __restrict__ src,
+                                            uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
+                                            int* s_tok) {
+  constexpr int NCP = 2 * MT;  // activation copies per wave per step (4 rows each)
+  const int K = GATE_UP ? a.H : a.I;
+  const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
+  const int nk = pack_steps(K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int row0 = bi.row0, rows = bi.rows;
+
+  const int c_first = bi.nt * (2 * kT4Waves) + wave * 2;
+  const bool active = c_first < nslices;
+  const int c0 = min(c_first, nslices - 2);
+  const size_t sstride = static_cast<size_t>(nk) * kPackBlock;
+
+  // Lane l reads column n = l mod 32 of the wave's 32-column tile: row
+  // n mod 16 of slice n/16; k-chunk j holds inputs 16j + 8h .. +7 (h = l/32),
+  // word j/2 of the 16 bytes at (16 (2 (j mod 2) + h) + row) * 16 of the
+  // packed block.
+  const int h = lane >> 5, nrow = lane & 15, nsl = (lane >> 4) & 1;
+  const uint8_t* cbase = bi.P + static_cast<size_t>(c0 + nsl) * sstride;
+  auto load_codes = [&](int s, RawCodes& rc) {
+    const uint8_t* blk = cbase + static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
+    rc.ce = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16);
+    rc.co = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16 + 512);
+    rc.g = *reinterpret_cast<const uint2*>(blk + kPackScales + nrow * 8);
+  };
+  auto to_tile = [&](const RawCodes& rc, TileCodes& tc) {
+    tc.q[0] = rc.ce.x; tc.q[1] = rc.co.x;
+    tc.q[2] = rc.ce.y; tc.q[3] = rc.co.y;
+    tc.q[4] = rc.ce.z; tc.q[5] = rc.co.z;
+    tc.q[6] = rc.ce.w; tc.q[7] = rc.co.w;
+    tc.sb[0] = rc.g.x;
+    tc.sb[1] = rc.g.y;
+  };
+  auto rebuild_j = [&](const TileCodes& tc, int j) -> bf16x8 {
+    const uint32_t sbw = tc.sb[j >> 2];
+    return as_bf16x8(dequant8_pairs(tc.q[j], bf16_to_f32(sbw & 0xFFFFu), bf16_to_f32(sbw >> 16)));
+  };
+
+  // Activation copies: copy i of wave w moves tile rows 4q .. 4q+3, q = 4i + w,
+  // into LDS bytes [1024 q, 1024 q + 1024); lane -> row 4q + lane/16, stored
+  // chunk lane % 16, which holds the row's chunk (lane % 16) ^ (row % 16).
+  const int cg = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
+  const uint16_t* arow[NCP];  // set once the block's tokens are known
+  auto issue_a = [&](int s, uint8_t* buf) {
+    const int kk = min(min(s, nk - 1) * kKS + cg * 8, K - 8);
+#pragma unroll
+    for (int i = 0; i < NCP; ++i)
+      __builtin_amdgcn_global_load_lds(arow[i] + kk, buf + (kT4Waves * i + wave) * 1024, 16, 0, 0);
+  };
+  const bool ktail = (K % kKS) != 0;
+  auto zero_tail = [&](int s, uint8_t* buf) {
+    if (ktail && s == nk - 1 && s * kKS + cg * 8 >= K) {
+#pragma unroll
+      for (int i = 0; i < NCP; ++i)
+        *reinterpret_cast<uint4*>(buf + (kT4Waves * i + wave) * 1024 + lane * 16) =
+            make_uint4(0, 0, 0, 0);
+    }
+  };
+  const int arow_l = lane & 31;
+  int aoff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) aoff[j] = arow_l * (kKS * 2) + (((2 * j + h) ^ (arow_l & 15)) * 16);
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
+
+  bf16x8 bq[2];
+  TileCodes tc;
+  auto step = [&](int s, uint8_t* acur, uint8_t* anew, RawCodes& rnext) {
+    wait_vmcnt<0>();  // activations of step s (and everything before)
+    zero_tail(s, acur);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(s + 1, rnext);
+    issue_a(s + 1, anew);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 af[2][MT];
+    auto read_a = [&](int j, bf16x8 (&f)[MT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        f[mt] = *reinterpret_cast<const bf16x8*>(acur + mt * 32 * (kKS * 2) + aoff[j]);
+    };
+    read_a(0, af[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < 7) read_a(j + 1, af[(j + 1) & 1]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bq[j & 1], acc[mt], 0, 0, 0);
+      if (j < 7) {
+        bq[(j + 1) & 1] = rebuild_j(tc, j + 1);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<NCP>();  // codes of step s+1
+        __builtin_amdgcn_sched_barrier(0);
+        to_tile(rnext, tc);
+        bq[0] = rebuild_j(tc, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The codes of step 0 do not depend on the block's tokens: they are in
+  // flight while the token list is gathered.
+  RawCodes r0, r1;
+  load_codes(0, r0);
+  if (GATE_UP) {
+    block_tokens(a, bi, s_tok);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int r = min(4 * (kT4Waves * i + wave) + (lane >> 4), rows - 1);
+    const int srow = GATE_UP ? max(s_tok[r], 0) : row0 + r;
+    arow[i] = src + static_cast<size_t>(srow) * K;
+  }
+  issue_a(0, As0);
+  wait_vmcnt<0>();
+  to_tile(r0, tc);
+  bq[0] = rebuild_j(tc, 0);
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    step(s, As0, As1, r1);
+    step(s + 1, As1, As0, r0);
+  }
+  if (s < nk) step(s, As0, As1, r1);
+  wait_vmcnt<0>();  // the last step's spare copies land before the LDS is released
+  if (!active) return;
+
+  const int n16 = lane & 15;
+  const int c = c_first + nsl;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+      const size_t r = static_cast<size_t>(row0 + m);
+      const float v = acc[mt][i];
+      if (GATE_UP) {
+        const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
+        if (n16 < 8 && m < rows) {
+          const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+          out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
+        }
+      } else if (m < rows) {
+        out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall4_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
+  __shared__ int s_tok[kTallM];
+
+  BlockInfo bi;
+  if (!block_info<GATE_UP>(a, bi, 2 * kT4Waves)) return;
+  if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
+  if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
+  switch ((bi.tm + 31) >> 5) {
+    case 1: tall4_block<1, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 2: tall4_block<2, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 3: tall4_block<3, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    default: tall4_block<4, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Short-batch kernel (every block at most 16 rows: decode and batches of up
 // to 16 tokens).  The weight stream is spread over the whole chip: a
 // workgroup of four waves covers 4/KS slices of one block, and each wave
@@ -861,6 +1063,11 @@ static hipError_t launch_gemv(const GemmArgs& a, const uint16_t* src, uint16_t* 
   return hipGetLastError();
 }
 
+#ifndef MOE_TALL4
+#define MOE_TALL4 1
+#endif
+constexpr bool kTall4 = MOE_TALL4;  // four-wave tall-tile kernel
+
 // Tall-tile kernel variant for a tile height bound (0: no tile exceeds kSmallM).
 int gemm_m_max_for(int tile_m_max) { return tile_m_max <= kSmallM ? 0 : 128; }
 
@@ -881,7 +1088,10 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
     hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP>), grid_small,
                        dim3(64 * kSmallWaves), 0, stream, ga, src, out);
   }
-  if (m_max) {
+  if (m_max && kTall4) {
+    const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4Waves)));
+    hipLaunchKernelGGL((w4_gemm_tall4_kernel<GATE_UP>), grid, dim3(kT4Threads), 0, stream, ga, src, out);
+  } else if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kTallWaves)));
     hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, ga, src, out);
   }
