@@ -802,6 +802,10 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bq[j & 1], acc[mt], 0, 0, 0);
       if (j < 7) {
         bq[(j + 1) & 1] = rebuild_j(tc, j + 1);
+        // The operand of the MFMAs above stays live past the rebuild, so the
+        // rebuild writes other registers and need not wait for those MFMAs
+        // to read theirs.
+        asm volatile("" ::"v"(bq[j & 1]));
       } else {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<NCP>();  // codes of step s+1
