@@ -703,7 +703,7 @@ struct RawCodes {
   uint2 g;
 };
 
-template <int MT, bool GATE_UP>
+template <int MT, int CT, bool GATE_UP>
 __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
@@ -716,22 +716,28 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
   const int wave = uniform(tid >> 6);
   const int row0 = bi.row0, rows = bi.rows;
 
-  const int c_first = bi.nt * (2 * kT4Waves) + wave * 2;
-  const bool active = c_first < nslices;
-  const int c0 = min(c_first, nslices - 2);
+  // CT 32-column tiles (two slices each) per wave; nslices is even, so a
+  // tile's two slices are both in or both out
+  const int c_first = bi.nt * (2 * CT * kT4Waves) + wave * 2 * CT;
   const size_t sstride = static_cast<size_t>(nk) * kPackBlock;
 
-  // Lane l reads column n = l mod 32 of the wave's 32-column tile: row
+  // Lane l reads column n = l mod 32 of each of its 32-column tiles: row
   // n mod 16 of slice n/16; k-chunk j holds inputs 16j + 8h .. +7 (h = l/32),
   // word j/2 of the 16 bytes at (16 (2 (j mod 2) + h) + row) * 16 of the
   // packed block.
   const int h = lane >> 5, nrow = lane & 15, nsl = (lane >> 4) & 1;
-  const uint8_t* cbase = bi.P + static_cast<size_t>(c0 + nsl) * sstride;
-  auto load_codes = [&](int s, RawCodes& rc) {
-    const uint8_t* blk = cbase + static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
-    rc.ce = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16);
-    rc.co = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16 + 512);
-    rc.g = *reinterpret_cast<const uint2*>(blk + kPackScales + nrow * 8);
+  const uint8_t* cbase[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    cbase[ct] = bi.P + static_cast<size_t>(min(c_first + 2 * ct, nslices - 2) + nsl) * sstride;
+  auto load_codes = [&](int s, RawCodes (&rc)[CT]) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const uint8_t* blk = cbase[ct] + static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
+      rc[ct].ce = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16);
+      rc[ct].co = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16 + 512);
+      rc[ct].g = *reinterpret_cast<const uint2*>(blk + kPackScales + nrow * 8);
+    }
   };
   auto to_tile = [&](const RawCodes& rc, TileCodes& tc) {
     tc.q[0] = rc.ce.x; tc.q[1] = rc.co.x;
@@ -771,15 +777,17 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
 #pragma unroll
   for (int j = 0; j < 8; ++j) aoff[j] = arow_l * (kKS * 2) + (((2 * j + h) ^ (arow_l & 15)) * 16);
 
-  f32x16 acc[MT];
+  f32x16 acc[CT][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[ct][mt][i] = 0.0f;
 
-  bf16x8 bq[2];
-  TileCodes tc;
-  auto step = [&](int s, uint8_t* acur, uint8_t* anew, RawCodes& rnext) {
+  bf16x8 bq[2][CT];
+  TileCodes tc[CT];
+  auto step = [&](int s, uint8_t* acur, uint8_t* anew, RawCodes (&rnext)[CT]) {
     wait_vmcnt<0>();  // activations of step s (and everything before)
     zero_tail(s, acur);
     lds_barrier();
@@ -798,20 +806,29 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
     for (int j = 0; j < 8; ++j) {
       if (j < 7) read_a(j + 1, af[(j + 1) & 1]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bq[j & 1], acc[mt], 0, 0, 0);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[ct][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bq[j & 1][ct],
+                                                               acc[ct][mt], 0, 0, 0);
       if (j < 7) {
-        bq[(j + 1) & 1] = rebuild_j(tc, j + 1);
-        // The operand of the MFMAs above stays live past the rebuild, so the
-        // rebuild writes other registers and need not wait for those MFMAs
-        // to read theirs.
-        asm volatile("" ::"v"(bq[j & 1]));
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          bq[(j + 1) & 1][ct] = rebuild_j(tc[ct], j + 1);
+          // The operand of the MFMAs above stays live past the rebuild, so
+          // the rebuild writes other registers and need not wait for those
+          // MFMAs to read theirs.
+          asm volatile("" ::"v"(bq[j & 1][ct]));
+        }
       } else {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<NCP>();  // codes of step s+1
         __builtin_amdgcn_sched_barrier(0);
-        to_tile(rnext, tc);
-        bq[0] = rebuild_j(tc, 0);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          to_tile(rnext[ct], tc[ct]);
+          bq[0][ct] = rebuild_j(tc[ct], 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -819,7 +836,7 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
 
   // The codes of step 0 do not depend on the block's tokens: they are in
   // flight while the token list is gathered.
-  RawCodes r0, r1;
+  RawCodes r0[CT], r1[CT];
   load_codes(0, r0);
   if (GATE_UP) {
     block_tokens(a, bi, s_tok);
@@ -833,8 +850,11 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
   }
   issue_a(0, As0);
   wait_vmcnt<0>();
-  to_tile(r0, tc);
-  bq[0] = rebuild_j(tc, 0);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    to_tile(r0[ct], tc[ct]);
+    bq[0][ct] = rebuild_j(tc[ct], 0);
+  }
   int s = 0;
   for (; s + 1 < nk; s += 2) {
     step(s, As0, As1, r1);
@@ -842,29 +862,38 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
   }
   if (s < nk) step(s, As0, As1, r1);
   wait_vmcnt<0>();  // the last step's spare copies land before the LDS is released
-  if (!active) return;
 
   const int n16 = lane & 15;
-  const int c = c_first + nsl;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int ct = 0; ct < CT; ++ct) {
+    const int ctile = c_first + 2 * ct;
+    if (ctile >= nslices) break;
+    const int c = ctile + nsl;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-      const size_t r = static_cast<size_t>(row0 + m);
-      const float v = acc[mt][i];
-      if (GATE_UP) {
-        const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
-        if (n16 < 8 && m < rows) {
-          const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
-          out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const size_t r = static_cast<size_t>(row0 + m);
+        const float v = acc[ct][mt][i];
+        if (GATE_UP) {
+          const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
+          if (n16 < 8 && m < rows) {
+            const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+            out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
+          }
+        } else if (m < rows) {
+          out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
         }
-      } else if (m < rows) {
-        out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
       }
     }
   }
 }
+
+#ifndef MOE_T4CT
+#define MOE_T4CT 2
+#endif
+constexpr int kT4CT = MOE_T4CT;  // 32-column tiles per wave of the four-wave kernel
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall4_kernel(
@@ -874,14 +903,14 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ int s_tok[kTallM];
 
   BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi, 2 * kT4Waves)) return;
+  if (!block_info<GATE_UP>(a, bi, 2 * kT4CT * kT4Waves)) return;
   if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
   switch ((bi.tm + 31) >> 5) {
-    case 1: tall4_block<1, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
-    case 2: tall4_block<2, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
-    case 3: tall4_block<3, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
-    default: tall4_block<4, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 1: tall4_block<1, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 2: tall4_block<2, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 3: tall4_block<3, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    default: tall4_block<4, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
   }
 }
 
@@ -1093,7 +1122,7 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
                        dim3(64 * kSmallWaves), 0, stream, ga, src, out);
   }
   if (m_max && kTall4) {
-    const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4Waves)));
+    const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4CT * kT4Waves)));
     hipLaunchKernelGGL((w4_gemm_tall4_kernel<GATE_UP>), grid, dim3(kT4Threads), 0, stream, ga, src, out);
   } else if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kTallWaves)));
