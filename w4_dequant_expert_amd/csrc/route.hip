@@ -533,24 +533,27 @@ __device__ void finish_tables(int T, int E, int k, int n_shared, int tile_m_max,
                               int cnt, int* s_cnt, int* s_off, int* s_bstart, int* tmp,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                               int32_t* __restrict__ blocks, int32_t* __restrict__ n_blocks,
-                              int max_blocks, uint32_t* __restrict__ status) {
+                              int max_blocks, uint32_t* __restrict__ status, bool write = true) {
   const int tid = threadIdx.x;
   const int S = T * k;
   int total = 0;
   const int off = block_exclusive_scan((tid < E) ? cnt : 0, tmp, &total);
   if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
+    if (write) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
     s_off[tid] = off;
     s_cnt[tid] = cnt;
   }
   if (tid == 0) {
-    offsets[E] = total;
+    if (write) offsets[E] = total;
     s_off[E] = S;
     s_cnt[E] = n_shared ? T : 0;
-    if (total != S) status_set(status, MOE_STATUS_BAD_INDEX);
+    if (write && total != S) status_set(status, MOE_STATUS_BAD_INDEX);
   }
   __syncthreads();
+  if (!write) return;  // only the offsets are needed
 
   // block map: blocks per group, scanned into each group's first block
   const int groups = E + (n_shared ? 1 : 0);
@@ -770,11 +773,15 @@ __global__ __launch_bounds__(1024) void route_scan_lds_kernel(
   const int S = T * k;
   const int W = (T + 31) / 32;
   const int nw = W * E;
+  // Every workgroup builds the same prefixes and offsets from the bitmask;
+  // workgroup 0 writes the tables, and each scatters its own range of slots.
+  const int slo = static_cast<int>(static_cast<long long>(blockIdx.x) * S / gridDim.x);
+  const int shi = static_cast<int>(static_cast<long long>(blockIdx.x + 1) * S / gridDim.x);
 
   // the first scatter round's slot experts, then the whole bitmask
   int ex[kScatterU];
 #pragma unroll
-  for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(tid + u * 1024, S - 1)];
+  for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(slo + tid + u * 1024, S - 1)];
   uint32_t bv[kScanLoads];
 #pragma unroll
   for (int u = 0; u < kScanLoads; ++u) bv[u] = bits[min(tid + u * 1024, nw - 1)];
@@ -809,19 +816,19 @@ __global__ __launch_bounds__(1024) void route_scan_lds_kernel(
     }
   }
   finish_tables(T, E, k, n_shared, tile_m_max, tile_gran, cnt, s_cnt, s_off, s_bstart, tmp, counts,
-                offsets, blocks, n_blocks, max_blocks, status);
+                offsets, blocks, n_blocks, max_blocks, status, blockIdx.x == 0);
   __syncthreads();  // s_pref complete
 
   // stable scatter: row = expert offset + tokens before t that chose e
-  for (int s0 = tid; s0 < S; s0 += kScatterU * 1024) {
-    if (s0 != tid) {
+  for (int s0 = slo + tid; s0 < shi; s0 += kScatterU * 1024) {
+    if (s0 != slo + tid) {
 #pragma unroll
       for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(s0 + u * 1024, S - 1)];
     }
 #pragma unroll
     for (int u = 0; u < kScatterU; ++u) {
       const int sl = s0 + u * 1024;
-      if (sl >= S) continue;
+      if (sl >= shi) continue;
       if (ex[u] < 0 || ex[u] >= E) {
         status_set(status, MOE_STATUS_BAD_INDEX);
         continue;
@@ -954,7 +961,9 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
     hipLaunchKernelGGL((router_topk_kernel<64>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
                        rb.topk_idx, rb.topk_w, rb.bits, rb.status);
   if (static_cast<long long>((T + 31) / 32) * E <= kScanLdsWords) {
-    hipLaunchKernelGGL(route_scan_lds_kernel, dim3(1), dim3(1024), 0, stream, T, E, k, d.n_shared,
+    // the scatter spread over up to eight workgroups (one per 2048 slots)
+    const int gs = max(1, min(8, T * k / 2048));
+    hipLaunchKernelGGL(route_scan_lds_kernel, dim3(gs), dim3(1024), 0, stream, T, E, k, d.n_shared,
                        d.tile_m_max, d.tile_gran, rb.bits, rb.counts, rb.offsets, rb.topk_idx,
                        rb.sorted_slot, rb.slot_pos, rb.blocks, rb.n_blocks, rb.max_blocks,
                        rb.status);
