@@ -388,36 +388,33 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ---------------------------------------------------------------------------
-// Tall-tile kernel: blocks of 48..128 rows (and, for large batches, every
-// block), computed as MT = 1..4 row tiles of 32 with v_mfma_f32_32x32x16_bf16
-// (on gfx950 the 32x32 form delivers twice the 16x16 form's throughput).  Eight waves, two per SIMD: each owns two
-// weight slices (one 32-column tile) and all of the block's rows, so each
-// rebuilt weight feeds MT MFMAs, and the two waves of a SIMD overlap each
-// other's matrix, vector and LDS work (one wave per SIMD leaves the matrix
-// core and LDS about half used).
-//   - Activations and packed codes are copied from memory straight into LDS
-//     (global_load_lds) two steps ahead, through three rotating buffers.
-//     A row's sixteen 16-byte chunks are stored XOR-swizzled by the row
-//     index, so rows need no padding and the MFMA reads are conflict-free.
-//   - The weights of MFMA k-chunk j+1 are rebuilt while the MFMAs of chunk j
-//     run; the codes of a step are read from LDS into registers at the end
-//     of the previous step.
-//   - The step loop has no divergent branches: a wave past the last slice
-//     (partial N tile) computes on a clamped slice and stores nothing; rows
-//     past the block copy a real row whose outputs are dropped; inputs past K
-//     are zeroed in LDS once their copy has landed.
+// Tall-tile kernel (blocks of 48..128 rows, and every block for large
+// batches): MT = 1..4 row tiles of 32 rows on v_mfma_f32_32x32x16_bf16 (on
+// gfx950 the 32x32 form delivers twice the 16x16 form's throughput).  A
+// workgroup of four waves covers 16 slices; each wave owns two 32-column
+// tiles and all of the block's rows, so each rebuilt weight feeds MT MFMAs
+// and each activation fragment read from LDS feeds 2 MT.
+//   - Only two activation buffers live in LDS (64 KB) and the weight codes go
+//     straight into registers, so two workgroups share a CU.  Each SIMD then
+//     holds waves of two workgroups whose step barriers, prologues and
+//     epilogues fall at different times, and one workgroup's waits are covered
+//     by the other's work (an eight-wave workgroup holding the whole LDS kept
+//     all of a CU's waves in lock-step and was about 10 % slower).
+//   - Step s issues the codes of step s+1 (registers), then the activations of
+//     step s+1 (copied from memory straight into LDS with global_load_lds,
+//     into the buffer step s-1 read, free after step s's barrier).  Before the
+//     last k-chunk of step s, all but the last NCP loads done means the codes
+//     of step s+1 have landed; at the start of step s+1 everything is waited
+//     for.  The step barrier is an s_barrier without the fence that would also
+//     drain copies still in flight.
+//   - A row's sixteen 16-byte chunks are stored XOR-swizzled by the row index,
+//     so rows need no padding and the 32-row MFMA reads are conflict-free.
+//   - The weights of k-chunk j+1 are rebuilt while the MFMAs of chunk j run.
 // MFMA operand convention (32x32x16): lane l supplies row l mod 32 of A and
 // column l mod 32 of B with eight consecutive reduction elements; in k-chunk
 // j of a step (j = 0..7) lane l carries inputs 16j + 8*(l/32) .. +7.  Lane l
 // receives D column l mod 32, rows 8*(i/4) + 4*(l/32) + (i mod 4), i = 0..15.
 // ---------------------------------------------------------------------------
-constexpr int kTallM = 128;
-constexpr int kTallWaves = 8;
-constexpr int kTallThreads = kTallWaves * kWave;
-constexpr int kTallBuf = kTallM * kKS * 2;      // bytes of one staged activation step
-constexpr int kCodeSlot = 1280;                 // LDS bytes per (slice, step): 1024 codes + 256
-constexpr int kCodeBuf = kTallWaves * 2 * kCodeSlot;  // one step's codes, two slices a wave
-
 // Workgroup barrier for LDS data whose copies the caller has already waited
 // for.  A plain __syncthreads() would also wait for every copy into LDS still
 // in flight (the prefetch of later steps); the asm's memory clobber keeps the
@@ -426,18 +423,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 32-bit LDS address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
-}
-
 // s_waitcnt vmcnt(N), leaving the other counters alone.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+constexpr int kTallM = 128;
+constexpr int kTallBuf = kTallM * kKS * 2;  // bytes of one staged activation step
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -448,253 +442,6 @@ struct TileCodes {
   uint32_t sb[2];
 };
 
-template <int MT, bool GATE_UP>
-__device__ __forceinline__ void tall_block(const GemmArgs& a, const BlockInfo& bi,
-                                           const uint16_t* __restrict__ src,
-                                           uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
-                                           uint8_t* As2, uint8_t* Cs0, uint8_t* Cs1, uint8_t* Cs2,
-                                           int* s_tok) {
-  constexpr int NCP = MT;  // activation copies per wave per step (4 rows each)
-  const int K = GATE_UP ? a.H : a.I;
-  const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
-  const int nk = pack_steps(K);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int row0 = bi.row0, rows = bi.rows;
-
-  // nslices is even, so a wave's two slices are both in or both out
-  const int c_first = bi.nt * 16 + wave * 2;
-  const bool active = c_first < nslices;
-  const int c0 = min(c_first, nslices - 2);
-  const uint8_t* sbase = bi.P + static_cast<size_t>(c0) * nk * kPackBlock;
-  const size_t sstride = static_cast<size_t>(nk) * kPackBlock;
-
-  // Activation copies: copy i of wave w moves tile rows 4q .. 4q+3, q = 8i + w,
-  // into LDS bytes [1024 q, 1024 q + 1024); lane -> row 4q + lane/16, stored
-  // chunk lane % 16, which holds the row's chunk cg = (lane % 16) ^ (row % 16).
-  const int cg = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
-  const uint16_t* arow[NCP];  // set once the block's tokens are known
-  auto issue_a = [&](int s, uint8_t* buf) {
-    const int kk = min(min(s, nk - 1) * kKS + cg * 8, K - 8);
-#pragma unroll
-    for (int i = 0; i < NCP; ++i)
-      __builtin_amdgcn_global_load_lds(arow[i] + kk, buf + (kTallWaves * i + wave) * 1024, 16, 0, 0);
-  };
-  const bool ktail = (K % kKS) != 0;
-  // after step s's copy has landed: zero the chunks past K (last step only)
-  auto zero_tail = [&](int s, uint8_t* buf) {
-    if (ktail && s == nk - 1 && s * kKS + cg * 8 >= K) {
-#pragma unroll
-      for (int i = 0; i < NCP; ++i)
-        *reinterpret_cast<uint4*>(buf + (kTallWaves * i + wave) * 1024 + lane * 16) =
-            make_uint4(0, 0, 0, 0);
-    }
-  };
-  // Code copies of one step for this wave's two slices (four copies): each
-  // slice's 1024 code bytes (16 a lane), then its 128 scale/bias bytes (4 a
-  // lane, the upper half of the wave repeating the lower half so nothing is
-  // read past the block) into this wave's slots of a code buffer.
-  const int cw = wave * (2 * kCodeSlot);
-  auto issue_codes = [&](int s, uint8_t* cbuf) {
-    const size_t off = static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-      const uint8_t* blk = sbase + ns * sstride + off;
-      __builtin_amdgcn_global_load_lds(blk + lane * 16, cbuf + cw + ns * kCodeSlot, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(blk + kPackScales + (lane & 31) * 4,
-                                       cbuf + cw + ns * kCodeSlot + 1024, 4, 0, 0);
-    }
-  };
-  // Lane l reads column n = l mod 32 of the tile, i.e. row n mod 16 of slice
-  // n/16.  k-chunk j holds inputs 16j + 8h .. +7 (h = l/32) of that row: in
-  // the packed block, word j/2 of the 16 bytes at (16 (2 (j mod 2) + h) +
-  // row) * 16, so the step's codes are two 16-byte reads, and the row's two
-  // scale/bias words are adjacent.  The codes of a step are read in one asm
-  // block that ends with its own lgkmcnt wait: the compiler cannot tell which
-  // of the copies in flight such reads depend on and would otherwise wait for
-  // all of them; the explicit vmcnt waits before each call cover the copies
-  // they need.
-  const int h = lane >> 5, nrow = lane & 15, nsl = (lane >> 4) & 1;
-  auto read_codes = [&](const uint8_t* cbuf, TileCodes& tc) {
-    const uint8_t* slot = cbuf + cw + nsl * kCodeSlot;
-    const uint32_t ac = lds_addr(slot + (16 * h + nrow) * 16);
-    const uint32_t as = lds_addr(slot + kPackScales + nrow * 8);
-    u32x4 ce, co;
-    u32x2 g;
-    asm volatile(
-        "ds_read_b128 %0, %3\n\t"
-        "ds_read_b128 %1, %3 offset:512\n\t"
-        "ds_read_b64 %2, %4\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(ce), "=&v"(co), "=&v"(g)
-        : "v"(ac), "v"(as));
-    tc.q[0] = ce.x; tc.q[1] = co.x;
-    tc.q[2] = ce.y; tc.q[3] = co.y;
-    tc.q[4] = ce.z; tc.q[5] = co.z;
-    tc.q[6] = ce.w; tc.q[7] = co.w;
-    tc.sb[0] = g.x;
-    tc.sb[1] = g.y;
-  };
-  // weights of k-chunk j of the tile
-  auto rebuild_j = [&](const TileCodes& tc, int j) -> bf16x8 {
-    const uint32_t sbw = tc.sb[j >> 2];
-    return as_bf16x8(dequant8_pairs(tc.q[j], bf16_to_f32(sbw & 0xFFFFu), bf16_to_f32(sbw >> 16)));
-  };
-  // LDS byte offset of this lane's A fragment for k-chunk j within a 32-row tile
-  const int arow_l = lane & 31;
-  int aoff[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) aoff[j] = arow_l * (kKS * 2) + (((2 * j + h) ^ (arow_l & 15)) * 16);
-
-  f32x16 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
-
-  // Every global load of the step loop is a copy into LDS; step s issues the
-  // activations of step s+2 (MT copies), then the codes of step s+2 (four
-  // copies), into the third of three rotating buffers.  So "all but the last
-  // MT + 4 copies done" at the start of step s means the activations and
-  // codes of step s have landed, and before the last k-chunk of step s it
-  // means the codes of step s+1 have.  The scheduling barriers keep the
-  // copies in program order around those waits.  The buffers are separate
-  // LDS arrays selected at compile time (the loop body is three steps), so
-  // the compiler sees which copies an activation read depends on; the codes
-  // of step s are read into registers at the end of step s-1.
-  constexpr int kInFlight = MT + 4;
-  bf16x8 bq[2];  // rebuilt weights of two k-chunks
-  TileCodes tc;  // codes of the current step
-  auto step = [&](int s, uint8_t* acur, uint8_t* anew, uint8_t* cnext, uint8_t* cnew) {
-    wait_vmcnt<kInFlight>();
-    zero_tail(s, acur);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(s + 2, anew);
-    issue_codes(s + 2, cnew);
-    __builtin_amdgcn_sched_barrier(0);
-    // A fragments are read one k-chunk ahead; each chunk's work is fenced off
-    // from the next, which bounds the live registers.
-    bf16x8 af[2][MT];
-    auto read_a = [&](int j, bf16x8 (&f)[MT]) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        f[mt] = *reinterpret_cast<const bf16x8*>(acur + mt * 32 * (kKS * 2) + aoff[j]);
-    };
-    read_a(0, af[0]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < 7) read_a(j + 1, af[(j + 1) & 1]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][mt], bq[j & 1], acc[mt], 0, 0, 0);
-      if (j < 7) {
-        bq[(j + 1) & 1] = rebuild_j(tc, j + 1);
-      } else {
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<kInFlight>();
-        __builtin_amdgcn_sched_barrier(0);
-        read_codes(cnext, tc);
-        bq[0] = rebuild_j(tc, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // The codes of steps 0 and 1 do not depend on the block's tokens: they are
-  // in flight while the token list is gathered.  Then the activations of
-  // steps 0 and 1; waiting for all but the last NCP copies leaves only the
-  // activations of step 1 in flight, which re-establishes the loop's
-  // invariant (the copies of step s have landed at its start).
-  issue_codes(0, Cs0);
-  issue_codes(1, Cs1);
-  if (GATE_UP) {
-    block_tokens(a, bi, s_tok);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < NCP; ++i) {
-    const int r = min(4 * (kTallWaves * i + wave) + (lane >> 4), rows - 1);
-    const int srow = GATE_UP ? max(s_tok[r], 0) : row0 + r;
-    arow[i] = src + static_cast<size_t>(srow) * K;
-  }
-  issue_a(0, As0);
-  issue_a(1, As1);
-  wait_vmcnt<NCP>();  // codes of steps 0 and 1, activations of step 0
-  read_codes(Cs0, tc);
-  bq[0] = rebuild_j(tc, 0);
-  int s = 0;
-  for (; s + 2 < nk; s += 3) {
-    step(s, As0, As2, Cs1, Cs2);
-    step(s + 1, As1, As0, Cs2, Cs0);
-    step(s + 2, As2, As1, Cs0, Cs1);
-  }
-  if (s < nk) step(s, As0, As2, Cs1, Cs2);
-  if (s + 1 < nk) step(s + 1, As1, As0, Cs2, Cs0);
-  if (!active) return;
-
-  const int n16 = lane & 15;
-  const int c = c_first + nsl;  // slice of this lane's column
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-      const size_t r = static_cast<size_t>(row0 + m);
-      const float v = acc[mt][i];
-      if (GATE_UP) {
-        const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
-        if (n16 < 8 && m < rows) {
-          const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
-          out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
-        }
-      } else if (m < rows) {
-        out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
-      }
-    }
-  }
-}
-
-template <bool GATE_UP>
-__global__ __launch_bounds__(kTallThreads) void w4_gemm_tall_kernel(GemmArgs a,
-                                                                    const uint16_t* __restrict__ src,
-                                                                    uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t As2[kTallBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t Cs0[kCodeBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t Cs1[kCodeBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t Cs2[kCodeBuf];
-  __shared__ int s_tok[kTallM];
-
-  BlockInfo bi;
-  if (!block_info<GATE_UP>(a, bi, 2 * kTallWaves)) return;
-  if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
-  if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
-  switch ((bi.tm + 31) >> 5) {
-    case 1: tall_block<1, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
-    case 2: tall_block<2, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
-    case 3: tall_block<3, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
-    default: tall_block<4, GATE_UP>(a, bi, src, out, As0, As1, As2, Cs0, Cs1, Cs2, s_tok); break;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Four-wave tall-tile kernel: the same tiles and MFMA layout as the
-// eight-wave kernel above, but a workgroup covers 8 slices (128 columns) with
-// four waves, keeps only two activation buffers in LDS (64 KB) and loads the
-// weight codes straight into registers, so two workgroups share a CU.  Each
-// SIMD then holds waves of two workgroups whose step barriers, prologues and
-// epilogues fall at different times, and one workgroup's waits are covered
-// by the other's work; the price is that a block's activation rows are
-// staged by twice as many workgroups.  Both kernels own the same blocks; the
-// host launches one of them.
-//   Step s issues the codes of step s+1 (registers), then the activations of
-//   step s+1 (LDS, the buffer step s-1 read, free after step s's barrier).
-//   Before the last k-chunk of step s, all but the last NCP loads done means
-//   the codes of step s+1 have landed; at the start of step s+1 everything is
-//   waited for.
-// ---------------------------------------------------------------------------
 constexpr int kT4Waves = 4;
 constexpr int kT4Threads = kT4Waves * kWave;
 
@@ -1084,22 +831,23 @@ static hipError_t launch_gemv(const GemmArgs& a, const uint16_t* src, uint16_t* 
   const dim3 grid(static_cast<unsigned>(a.max_blocks) * ((nslices + spw - 1) / spw));
 #define MOE_GEMV(KS, ONE) \
   hipLaunchKernelGGL((w4_gemv_kernel<KS, GATE_UP, ONE>), grid, dim3(256), 0, stream, a, src, out)
-  const bool one = GATE_UP && a.T == 1;
-  if (ks == 4) {
-    if (one) MOE_GEMV(4, true); else MOE_GEMV(4, false);
-  } else if (ks == 2) {
-    if (one) MOE_GEMV(2, true); else MOE_GEMV(2, false);
+  if constexpr (GATE_UP) {
+    const bool one = a.T == 1;
+    if (ks == 4) {
+      if (one) MOE_GEMV(4, true); else MOE_GEMV(4, false);
+    } else if (ks == 2) {
+      if (one) MOE_GEMV(2, true); else MOE_GEMV(2, false);
+    } else {
+      if (one) MOE_GEMV(1, true); else MOE_GEMV(1, false);
+    }
   } else {
-    if (one) MOE_GEMV(1, true); else MOE_GEMV(1, false);
+    if (ks == 4) MOE_GEMV(4, false);
+    else if (ks == 2) MOE_GEMV(2, false);
+    else MOE_GEMV(1, false);
   }
 #undef MOE_GEMV
   return hipGetLastError();
 }
-
-#ifndef MOE_TALL4
-#define MOE_TALL4 1
-#endif
-constexpr bool kTall4 = MOE_TALL4;  // four-wave tall-tile kernel
 
 // Tall-tile kernel variant for a tile height bound (0: no tile exceeds kSmallM).
 int gemm_m_max_for(int tile_m_max) { return tile_m_max <= kSmallM ? 0 : 128; }
@@ -1121,12 +869,9 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
     hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP>), grid_small,
                        dim3(64 * kSmallWaves), 0, stream, ga, src, out);
   }
-  if (m_max && kTall4) {
+  if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4CT * kT4Waves)));
     hipLaunchKernelGGL((w4_gemm_tall4_kernel<GATE_UP>), grid, dim3(kT4Threads), 0, stream, ga, src, out);
-  } else if (m_max) {
-    const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kTallWaves)));
-    hipLaunchKernelGGL((w4_gemm_tall_kernel<GATE_UP>), grid, dim3(kTallThreads), 0, stream, ga, src, out);
   }
   return hipGetLastError();
 }
