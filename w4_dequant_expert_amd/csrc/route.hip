@@ -158,8 +158,24 @@ __global__ __launch_bounds__(WT * WE * 64) void router_scores_kernel(
   // lower half of its outputs and the partner keeps the upper half; each adds
   // its partner's copy.  Tree index of lane L is L mod 2s, so the pairing is
   // p[i] + p[i+s].  After s = 1 lane L holds output L.
+  // At s = 32 and 16 one v_permlane32_swap / v_permlane16_swap of the pair
+  // (acc[i], acc[i+s]) leaves, in every lane, its own kept value in one
+  // register and the partner's in the other, so the level is one swap and one
+  // add per output (the same sum: addition commutes).
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i + 32]),
+                                                    false, false);
+    acc[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i + 16]),
+                                                    false, false);
+    acc[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) {
     const bool upper = (lane & s) != 0;
 #pragma unroll
     for (int i = 0; i < s; ++i) {
