@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_prefill512.txt")
-DOMINANT = "w4_gemm_small_kernel<4, 2, true>"   # the gate/up GEMM of the 512-token workload
+DOMINANT = "w4_gemm_small_kernel<4, 2, true, 0>"   # the gate/up GEMM of the 512-token workload
 # Tile height bound per workload: uniform routing at 512 tokens gives every
 # expert 7-27 rows, so 32-row tiles cover them and the shared expert's 512
 # rows in 16 blocks; the skewed 2048-token batch has groups of up to ~2000

@@ -214,6 +214,30 @@ int moe_grouped_w4_ffn(const moe_dims *d, const uint16_t *x, const moe_route_out
                        uint16_t *y_slots, void *stream);
 
 /*
+ * Shared-expert overlap.  The shared expert processes every token regardless
+ * of routing [RL, "Understanding the Qwen3.6-35B-A3B Model"], so its FFN needs
+ * no routing tables and can run on a second stream while moe_route runs on
+ * the first.  The pair moe_shared_w4_ffn + moe_routed_w4_ffn writes exactly
+ * what moe_grouped_w4_ffn writes (bit for bit: the same kernels compute the
+ * same blocks); moe_combine then needs both done (an event from the second
+ * stream).
+ *
+ * moe_shared_w4_ffn - the shared expert's rows of h and y_slots (rows T*k ..
+ * T*k+T-1), from x and the shared bank alone.  Requires n_shared = 1
+ * (else MOE_EINVAL).  h, y_slots and x as for moe_grouped_w4_ffn.
+ */
+int moe_shared_w4_ffn(const moe_dims *d, const uint16_t *x, const moe_w4_bank *shared, uint16_t *h,
+                      uint16_t *y_slots, void *stream);
+
+/*
+ * moe_routed_w4_ffn - moe_grouped_w4_ffn without the shared expert's blocks:
+ * the routed rows 0 .. T*k-1 of h and y_slots.  The routing tables must come
+ * from moe_route on the same stream.
+ */
+int moe_routed_w4_ffn(const moe_dims *d, const uint16_t *x, const moe_route_out *r,
+                      const moe_w4_bank *routed, uint16_t *h, uint16_t *y_slots, void *stream);
+
+/*
  * moe_combine - weighted top-k combine [RL, "Understanding the Qwen3.6-35B-A3B
  * Model"]: y[t] = sum_j topk_w[t][j] * y_slots[slot_pos[t*k+j]]
  * (+ y_slots[T*k + t] when n_shared = 1), float32, j ascending, shared last,

@@ -112,6 +112,33 @@ def test_ffn_and_combine_validation_codes():
     assert L.moe_w4_dequant(0, 64, 0x1000, 0x2000, 0x3000, 0x4000, None) == 0
 
 
+def test_split_ffn_validation_codes():
+    L = moe.lib()
+    d = full(4)
+    out = _route_out()
+    bank = Bank(0x2000, 0x3000)
+    mis = Bank(0x2008, 0x3000)
+    # the shared-expert half: needs n_shared = 1, a bank and aligned buffers
+    d_noshared = moe.make_dims(4, 2048, 512, 256, 8, 0, 128, 16)
+    assert L.moe_shared_w4_ffn(ctypes.byref(d_noshared), 0x1000, ctypes.byref(bank), 0x8000,
+                               0x9000, None) == -1
+    assert L.moe_shared_w4_ffn(ctypes.byref(d), 0x1000, None, 0x8000, 0x9000, None) == -1
+    assert L.moe_shared_w4_ffn(ctypes.byref(d), 0x1000, ctypes.byref(mis), 0x8000, 0x9000, None) == -2
+    assert L.moe_shared_w4_ffn(ctypes.byref(d), 0x1000, ctypes.byref(bank), None, 0x9000, None) == -1
+    assert L.moe_shared_w4_ffn(ctypes.byref(d), 0x1008, ctypes.byref(bank), 0x8000, 0x9000, None) == -2
+    # the routed half: routing tables and the routed bank, no shared bank
+    assert L.moe_routed_w4_ffn(ctypes.byref(d), 0x1000, ctypes.byref(out), None, 0x8000, 0x9000,
+                               None) == -1
+    assert L.moe_routed_w4_ffn(ctypes.byref(d), 0x1000, None, ctypes.byref(bank), 0x8000, 0x9000,
+                               None) == -1
+    assert L.moe_routed_w4_ffn(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                               0x8000, 0x9004, None) == -2
+    d0 = full(0)
+    assert L.moe_shared_w4_ffn(ctypes.byref(d0), 0x1000, ctypes.byref(bank), 0x8000, 0x9000, None) == 0
+    assert L.moe_routed_w4_ffn(ctypes.byref(d0), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                               0x8000, 0x9000, None) == 0
+
+
 def test_pack_sizes_and_validation():
     L = moe.lib()
     # one 1152-byte block per (16-row slice, 128-input step)

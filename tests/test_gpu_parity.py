@@ -295,6 +295,44 @@ def test_grouped_ffn_matches_separate_calls(full_banks, T):
     assert torch.equal(layer.y_slots, ys_ref)
 
 
+@pytest.mark.parametrize("cfg,T,tile_m_max", [("decode1", 1, 32), ("decode1", 5, 32),
+                                               ("decode1", 48, 32), ("prefill512", 512, 32),
+                                               ("decode1", 300, 128), ("prefill2048_zipf", 2048, 128)])
+def test_split_ffn_matches_grouped(full_banks, cfg, T, tile_m_max):
+    """The shared expert on a second stream, concurrent with routing, then the
+    routed experts (moe_shared_w4_ffn + moe_routed_w4_ffn): h and y_slots equal
+    moe_grouped_w4_ffn's bit for bit, on three calls in a row, status clear."""
+    note(f"case split FFN {cfg} T={T} tile {tile_m_max}")
+    c = build_config(cfg, T=T, t0=100 if cfg == "decode1" else 0, with_weights=False)
+    sh = c["shape"]
+    routed_np, shared_np, routed_dev, shared_dev = full_banks
+    layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, routed_dev, shared_dev, c["wr"],
+                         c["bias"], T_max=T, tile_m_max=tile_m_max)
+    x = dev(c["x"])
+    d = layer.route(x)
+    layer.ffn(d, x)
+    torch.cuda.synchronize()
+    h_ref, ys_ref = layer.h.clone(), layer.y_slots.clone()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        layer.h.zero_()
+        layer.y_slots.zero_()
+        ready = torch.cuda.Event()
+        ready.record(main)
+        side.wait_event(ready)
+        layer.shared_ffn(d, x, stream=side)
+        d = layer.route(x, stream=main)
+        layer.routed_ffn(d, x, stream=main)
+        done = torch.cuda.Event()
+        done.record(side)
+        main.wait_event(done)
+        torch.cuda.synchronize()
+        assert int(layer.rt.status.item()) == 0, rep
+        assert torch.equal(layer.h, h_ref), rep
+        assert torch.equal(layer.y_slots, ys_ref), rep
+
+
 @pytest.mark.parametrize("tok", [0, 1, 999])
 def test_decode1_tokens(full_banks, tok):
     check_layer("decode1", T=1, t0=tok, banks=full_banks, label=f"decode token {tok}")

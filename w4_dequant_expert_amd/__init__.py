@@ -25,6 +25,8 @@ from .moe import (  # noqa: F401
     moe_max_blocks,
     moe_route,
     moe_route_ws_bytes,
+    moe_routed_w4_ffn,
+    moe_shared_w4_ffn,
     moe_w4_dequant,
     moe_w4_pack,
     moe_w4_packed_bytes,

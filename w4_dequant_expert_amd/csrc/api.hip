@@ -245,6 +245,55 @@ int moe_grouped_w4_ffn(const moe_dims* d, const uint16_t* x, const moe_route_out
   return launched(launch_down(a, m_max, h, y_slots, s));
 }
 
+int moe_routed_w4_ffn(const moe_dims* d, const uint16_t* x, const moe_route_out* r,
+                      const moe_w4_bank* routed, uint16_t* h, uint16_t* y_slots, void* stream) {
+  int rc = validate_dims(d);
+  if (rc) return rc;
+  if ((rc = validate_route_out(r, false))) return rc;
+  if ((rc = validate_bank(routed))) return rc;
+  if (!x || !h || !y_slots) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(y_slots, 16)) return MOE_EALIGN;
+  if (d->T == 0) return MOE_OK;
+  if ((rc = check_device())) return rc;
+  GemmArgs a = gemm_args(*d, r, routed, nullptr);
+  a.shared_mode = 1;
+  const int m_max = gemm_m_max_for(d->tile_m_max);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((rc = launched(launch_gate_up(a, m_max, x, h, s)))) return rc;
+  return launched(launch_down(a, m_max, h, y_slots, s));
+}
+
+int moe_shared_w4_ffn(const moe_dims* d, const uint16_t* x, const moe_w4_bank* shared, uint16_t* h,
+                      uint16_t* y_slots, void* stream) {
+  int rc = validate_dims(d);
+  if (rc) return rc;
+  if (d->n_shared != 1) return MOE_EINVAL;
+  if ((rc = validate_bank(shared))) return rc;
+  if (!x || !h || !y_slots) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(y_slots, 16)) return MOE_EALIGN;
+  if (d->T == 0) return MOE_OK;
+  if ((rc = check_device())) return rc;
+  // No routing tables: the shared group always holds all T rows.
+  GemmArgs a{};
+  a.T = d->T;
+  a.H = d->H;
+  a.I = d->I;
+  a.E = d->E;
+  a.k = d->k;
+  a.n_shared = 1;
+  a.max_blocks = max_blocks_of(*d);
+  a.shared = view(shared);
+  a.n_shared_blocks = (d->T + d->tile_m_max - 1) / d->tile_m_max;
+  a.tile_gran = d->tile_gran;
+  a.shared_mode = 2;
+  const int m_max = gemm_m_max_for(d->tile_m_max);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((rc = launched(launch_gate_up(a, m_max, x, h, s)))) return rc;
+  return launched(launch_down(a, m_max, h, y_slots, s));
+}
+
 int moe_combine(const moe_dims* d, const moe_route_out* r, const uint16_t* y_slots, uint16_t* y,
                 void* stream) {
   int rc = validate_dims(d);

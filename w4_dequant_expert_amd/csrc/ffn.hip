@@ -133,8 +133,10 @@ template <bool GATE_UP>
 __device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi, int spw) {
   const int ntiles = n_tiles<GATE_UP>(a, spw);
   const int r = blockIdx.x / kXcds;
-  const int bid = kXcds * (r / ntiles) + blockIdx.x % kXcds;
+  int bid = kXcds * (r / ntiles) + blockIdx.x % kXcds;
   bi.nt = r % ntiles;
+  // routed blocks only: the grid starts after the shared blocks
+  if (a.shared_mode == 1) bid += a.n_shared_blocks;
   // The shared expert's blocks, last in the map, are dealt first: they all
   // stream the same weights, and started together with the routed blocks
   // they no longer form the last, partly filled round of workgroups alone.
@@ -149,6 +151,7 @@ __device__ __forceinline__ bool block_info(const GemmArgs& a, BlockInfo& bi, int
     bi.tm = (bs + (rem > 0 ? 1 : 0) + a.tile_gran - 1) / a.tile_gran * a.tile_gran;
     return true;
   }
+  if (a.shared_mode == 2) return false;  // shared blocks only: no routing tables are read
   // A routed block: its entry is loaded together with the map length (the
   // index is in bounds either way), not after it.
   const int rb = bid - nsh;
@@ -374,7 +377,10 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   }
 }
 
-template <int WAVES, int SW, bool GATE_UP>
+// MODE: the blocks the launch computes (GemmArgs::shared_mode: 0 all, 1 the
+// routed ones, 2 the shared expert's), a kernel of its own per mode so that
+// traces tell the launches apart.
+template <int WAVES, int SW, bool GATE_UP, int MODE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
     GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
@@ -643,12 +649,9 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
 constexpr int kT4CT = MOE_T4CT;  // 32-column tiles per wave of the four-wave kernel
 
 template <bool GATE_UP>
-__global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall4_kernel(
-    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
-  __shared__ int s_tok[kTallM];
-
+__device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* __restrict__ src,
+                                            uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
+                                            int* s_tok) {
   BlockInfo bi;
   if (!block_info<GATE_UP>(a, bi, 2 * kT4CT * kT4Waves)) return;
   if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
@@ -659,6 +662,36 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
     case 3: tall4_block<3, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
     default: tall4_block<4, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
   }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall4_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
+  __shared__ int s_tok[kTallM];
+  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
+}
+
+// The same kernel for the launches that compute only the routed blocks and only
+// the shared expert's blocks (kernels of their own, so that traces tell the
+// launches apart).
+template <bool GATE_UP>
+__global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall4_routed_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
+  __shared__ int s_tok[kTallM];
+  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall4_shared_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
+  __shared__ int s_tok[kTallM];
+  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -685,18 +718,23 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int ntiles = (nslices + SPW - 1) / SPW;
   const int bid = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
-  // bid < max_blocks (grid size): the entry is loaded together with the map
-  // length, not after it
-  const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
-  const int nblk = min(*a.n_blocks, a.max_blocks);
-  if (bid >= nblk) return;
   BlockInfo bi;
-  {
+  bi.nt = 0;
+  if (a.shared_mode == 2) {  // the shared expert only: one block of all T rows
+    bi.G = a.E;
+    bi.row0 = a.T * a.k;
+    bi.rows = a.T;
+    bi.tm = (a.T + a.tile_gran - 1) / a.tile_gran * a.tile_gran;
+  } else {
+    // bid < max_blocks (grid size): the entry is loaded together with the map
+    // length, not after it; the routed-only launch stops before the shared block
+    const int4 blk = reinterpret_cast<const int4*>(a.blocks)[bid];
+    const int nblk = min(*a.n_blocks, a.max_blocks) - (a.shared_mode == 1 ? a.n_shared_blocks : 0);
+    if (bid >= nblk) return;
     bi.G = blk.x;
     bi.row0 = blk.y;
     bi.rows = blk.z;
     bi.tm = blk.w;
-    bi.nt = 0;
   }
   if (bi.rows > kGemvRows) {  // the host launches this kernel only when T <= 16
     if (threadIdx.x == 0) status_set(a.status, MOE_STATUS_BAD_INDEX);
@@ -828,7 +866,9 @@ static hipError_t launch_gemv(const GemmArgs& a, const uint16_t* src, uint16_t* 
   // about four steps per wave: split the inputs of a slice over up to four waves
   const int ks = nk >= 16 ? 4 : nk >= 8 ? 2 : 1;
   const int spw = 4 / ks;
-  const dim3 grid(static_cast<unsigned>(a.max_blocks) * ((nslices + spw - 1) / spw));
+  const int nb = a.shared_mode == 2 ? 1 : a.max_blocks - (a.shared_mode == 1 ? a.n_shared_blocks : 0);
+  if (nb <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(nb) * ((nslices + spw - 1) / spw));
 #define MOE_GEMV(KS, ONE) \
   hipLaunchKernelGGL((w4_gemv_kernel<KS, GATE_UP, ONE>), grid, dim3(256), 0, stream, a, src, out)
   if constexpr (GATE_UP) {
@@ -856,7 +896,6 @@ template <bool GATE_UP>
 static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src, uint16_t* out,
                               hipStream_t stream) {
   if (a.T <= kGemvRows) return launch_gemv<GATE_UP>(a, src, out, stream);
-  const long long blocks8 = (a.max_blocks + kXcds - 1) / kXcds * kXcds;
   // When tall tiles are allowed and an expert averages at least kSmallM rows,
   // nearly all rows sit in tall blocks; the few short blocks then run in the
   // tall-tile kernel too (one 32-row tile), where they fill its last round of
@@ -864,14 +903,41 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
   // cannot fill.
   GemmArgs ga = a;
   ga.tall_all = m_max && static_cast<long long>(a.T) * a.k >= static_cast<long long>(kSmallM) * a.E;
+  const int nsh = a.n_shared_blocks;
+  if (a.shared_mode == 2) {  // the shared expert only: its tile height is known here
+    if (nsh <= 0) return hipSuccess;
+    const int tm = ((a.T + nsh - 1) / nsh + a.tile_gran - 1) / a.tile_gran * a.tile_gran;
+    const long long b8 = (nsh + kXcds - 1) / kXcds * kXcds;
+    if (tm <= kSmallM && !ga.tall_all) {
+      hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 2>),
+                         dim3(static_cast<unsigned>(b8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves))),
+                         dim3(64 * kSmallWaves), 0, stream, ga, src, out);
+    } else {
+      hipLaunchKernelGGL((w4_gemm_tall4_shared_kernel<GATE_UP>),
+                         dim3(static_cast<unsigned>(b8 * n_tiles<GATE_UP>(a, 2 * kT4CT * kT4Waves))),
+                         dim3(kT4Threads), 0, stream, ga, src, out);
+    }
+    return hipGetLastError();
+  }
+  const int nb = a.max_blocks - (a.shared_mode == 1 ? nsh : 0);
+  if (nb <= 0) return hipSuccess;
+  const long long blocks8 = (nb + kXcds - 1) / kXcds * kXcds;
+  const bool routed_only = a.shared_mode == 1;
   if (!ga.tall_all) {
     const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves)));
-    hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP>), grid_small,
-                       dim3(64 * kSmallWaves), 0, stream, ga, src, out);
+    if (routed_only)
+      hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 1>), grid_small,
+                         dim3(64 * kSmallWaves), 0, stream, ga, src, out);
+    else
+      hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 0>), grid_small,
+                         dim3(64 * kSmallWaves), 0, stream, ga, src, out);
   }
   if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4CT * kT4Waves)));
-    hipLaunchKernelGGL((w4_gemm_tall4_kernel<GATE_UP>), grid, dim3(kT4Threads), 0, stream, ga, src, out);
+    if (routed_only)
+      hipLaunchKernelGGL((w4_gemm_tall4_routed_kernel<GATE_UP>), grid, dim3(kT4Threads), 0, stream, ga, src, out);
+    else
+      hipLaunchKernelGGL((w4_gemm_tall4_kernel<GATE_UP>), grid, dim3(kT4Threads), 0, stream, ga, src, out);
   }
   return hipGetLastError();
 }

@@ -38,6 +38,7 @@ struct GemmArgs {
   int n_shared_blocks;  // blocks of the shared expert (the last ones of the map)
   int tile_gran;        // tile heights are multiples of this
   int tall_all;         // set by the launcher: the tall-tile kernel takes every block
+  int shared_mode;      // 0: every block; 1: the routed blocks only; 2: the shared blocks only
 };
 
 // M_MAX: largest tile height the chosen kernel variant accepts (64, 128, 256).

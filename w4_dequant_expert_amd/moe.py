@@ -20,8 +20,8 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWS, MOE_EDEVICE, MOE_ELAUNCH = 0, -1, -2, -
 STATUS_NAN_LOGIT, STATUS_BAD_INDEX, STATUS_BLOCK_OVERFLOW = 1, 2, 4
 
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_bytes", "moe_route",
-            "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_combine", "moe_w4_dequant",
-            "moe_w4_packed_bytes", "moe_w4_pack")
+            "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
+            "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_packed_bytes", "moe_w4_pack")
 
 
 class Dims(ctypes.Structure):
@@ -79,6 +79,10 @@ def lib():
         L.moe_w4_down.argtypes = [P(Dims), P(RouteOut), P(Bank), P(Bank), vp, vp, vp]
         L.moe_grouped_w4_ffn.restype = ctypes.c_int
         L.moe_grouped_w4_ffn.argtypes = [P(Dims), vp, P(RouteOut), P(Bank), P(Bank), vp, vp, vp]
+        L.moe_shared_w4_ffn.restype = ctypes.c_int
+        L.moe_shared_w4_ffn.argtypes = [P(Dims), vp, P(Bank), vp, vp, vp]
+        L.moe_routed_w4_ffn.restype = ctypes.c_int
+        L.moe_routed_w4_ffn.argtypes = [P(Dims), vp, P(RouteOut), P(Bank), vp, vp, vp]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [P(Dims), P(RouteOut), vp, vp, vp]
         L.moe_w4_dequant.restype = ctypes.c_int
@@ -155,6 +159,16 @@ def moe_grouped_w4_ffn(d: Dims, x, out: RouteOut, routed: Bank, shared, h, y_slo
                                     ctypes.byref(routed),
                                     ctypes.byref(shared) if shared is not None else None,
                                     _ptr(h), _ptr(y_slots), _stream(stream)), "moe_grouped_w4_ffn")
+
+
+def moe_shared_w4_ffn(d: Dims, x, shared: Bank, h, y_slots, stream=None):
+    _check(lib().moe_shared_w4_ffn(ctypes.byref(d), _ptr(x), ctypes.byref(shared), _ptr(h),
+                                   _ptr(y_slots), _stream(stream)), "moe_shared_w4_ffn")
+
+
+def moe_routed_w4_ffn(d: Dims, x, out: RouteOut, routed: Bank, h, y_slots, stream=None):
+    _check(lib().moe_routed_w4_ffn(ctypes.byref(d), _ptr(x), ctypes.byref(out), ctypes.byref(routed),
+                                   _ptr(h), _ptr(y_slots), _stream(stream)), "moe_routed_w4_ffn")
 
 
 def moe_combine(d: Dims, out: RouteOut, y_slots, y, stream=None):
@@ -324,6 +338,16 @@ class MoeLayer:
         s = shared or self.shared
         moe_grouped_w4_ffn(d, x, self.rt.c, r.c, s.c if s is not None else None, self.h,
                            self.y_slots, stream)
+
+    def shared_ffn(self, d, x, shared=None, stream=None):
+        """The shared expert's rows of h and y_slots; needs no routing."""
+        s = shared or self.shared
+        moe_shared_w4_ffn(d, x, s.c, self.h, self.y_slots, stream)
+
+    def routed_ffn(self, d, x, routed=None, stream=None):
+        """The routed rows of h and y_slots (after route on the same stream)."""
+        r = routed or self.routed
+        moe_routed_w4_ffn(d, x, self.rt.c, r.c, self.h, self.y_slots, stream)
 
     def combine(self, d, y, stream=None):
         moe_combine(d, self.rt.c, self.y_slots, y, stream)
