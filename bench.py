@@ -48,6 +48,8 @@ def parse():
                    help="largest GEMM tile height (default: per workload)")
     p.add_argument("--no-extra", action="store_true", help="skip the 2048-token, decode and chunked-prompt legs")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--overlap", action="store_true",
+                   help="run the shared expert's FFN on a second stream, concurrent with routing")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration)")
     p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1", "chunked16384"],
@@ -94,18 +96,40 @@ class Workload:
                                   T_max=max(self.T, 1), tile_m_max=tile_m_max, export_logits=False)
         self.x = torch.from_numpy(c["x"].view(np.int16)).to("cuda")
         self.y = torch.empty((self.T, sh.H), dtype=torch.int16, device="cuda")
+        # second stream (default priority) for the shared expert, and its events
+        self.side = torch.cuda.Stream()
+        self.ready = torch.cuda.Event()
+        self.done = torch.cuda.Event()
 
-    def step(self, i, ev=None, x=None):
-        """One layer call: route, gate/up, down, combine.  Untimed steps go
-        through the library's grouped FFN call; timed steps call gate/up and
-        down separately so that each stage has its own events."""
+    def step(self, i, ev=None, x=None, overlap=False):
+        """One layer call.  Without events: route, the grouped FFN call and
+        the combine on one stream; with overlap, the shared expert's FFN on a
+        second stream, concurrent with routing (it needs no routing tables),
+        the routed experts' FFN after routing, and the combine once both are
+        done.  With events (the stage breakdown): route, gate/up, down and
+        combine in sequence on one stream, each stage between its own events."""
+        import torch
         r, s, wr = self.copies[i % len(self.copies)]
         L = self.layer
         L.w_router = wr
         x = self.x if x is None else x
-        if ev is None:
+        if ev is None and not overlap:  # one stream, the grouped FFN call
             d = L.route(x)
             L.ffn(d, x, r, s)
+            L.combine(d, self.y)
+            return
+        if ev is None:
+            main = torch.cuda.current_stream()
+            if self.sh.n_shared:
+                # after the previous call's combine has read y_slots
+                self.ready.record(main)
+                self.side.wait_event(self.ready)
+                L.shared_ffn(L.dims(x.shape[0]), x, s, stream=self.side)
+            d = L.route(x)
+            L.routed_ffn(d, x, r)
+            if self.sh.n_shared:
+                self.done.record(self.side)
+                main.wait_event(self.done)
             L.combine(d, self.y)
             return
         ev[0].record()
@@ -138,19 +162,29 @@ class Workload:
         )
 
 
-def time_workload(wl, steps, warmup, fresh_tokens=None):
-    """Wall time of `steps` steps and per-stage HIP event durations (ms)."""
+TIMING_NOTE = ("tokens_per_s and ms_per_step: wall clock of whole layer calls (route, grouped "
+               "FFN, combine) with no events in between; stage times: further calls with each "
+               "stage between HIP events")
+
+
+def time_workload(wl, steps, warmup, fresh_tokens=None, overlap=False):
+    """Wall time of `steps` whole layer calls with no events in between
+    (overlap: the shared expert on a second stream), then per-stage HIP event
+    durations (ms) of `steps` more calls, in sequence on one stream."""
     import torch
+    tok = (lambda i: None) if fresh_tokens is None else (lambda i: fresh_tokens[i % len(fresh_tokens)])
     for i in range(warmup):
-        wl.step(i, x=None if fresh_tokens is None else fresh_tokens[i % len(fresh_tokens)])
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        wl.step(i, x=tok(i), overlap=overlap)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        wl.step(warmup + i, evs[i],
-                x=None if fresh_tokens is None else fresh_tokens[(warmup + i) % len(fresh_tokens)])
+        wl.step(warmup + i, x=tok(warmup + i), overlap=overlap)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        wl.step(warmup + steps + i, evs[i], x=tok(warmup + steps + i))
+    torch.cuda.synchronize()
     stage = [0.0] * 4
     for e in evs:
         for j in range(4):
@@ -196,10 +230,11 @@ def decode_leg(copies=40):
     fresh = [torch.from_numpy(make_tokens(1, 2048, 4, t0=i).view(np.int16)).to("cuda")
              for i in range(copies)]
     for i in range(5):
-        wl.step(i, x=fresh[i])
-    # eager steps (host launch overhead included) for reference
-    w_eager, _ = time_workload(wl, 200, 20, fresh)
-    step_ms = graph_ms(lambda i: wl.step(i, x=fresh[i]), copies)
+        wl.step(i, x=fresh[i], overlap=False)
+    # eager steps (host launch overhead included) for reference; one stream,
+    # as in the captured graph
+    w_eager, _ = time_workload(wl, 200, 20, fresh, overlap=False)
+    step_ms = graph_ms(lambda i: wl.step(i, x=fresh[i], overlap=False), copies)
     L = wl.layer
     d = L.dims(1)
     x0 = fresh[0]
@@ -373,7 +408,7 @@ def main():
         print(json.dumps({"chunked16384": chunked_leg(args.copies)}))
         return
     wl = Workload(main_name, args.copies, args.tile_m_max)
-    wall, stages = time_workload(wl, args.steps, args.warmup)
+    wall, stages = time_workload(wl, args.steps, args.warmup, overlap=args.overlap)
     work = wl.work()
     ms = wall / args.steps * 1e3
     tok_s = wl.T * args.steps / wall
@@ -383,7 +418,9 @@ def main():
     gemm_tflops = (work["flops_gate_up"] + work["flops_down"]) / (gu_s + dn_s) / 1e12
     gemm_gbs = (work["bytes_gate_up"] + work["bytes_down"]) / (gu_s + dn_s) / 1e9
     extra[main_name] = dict(
-        tokens_per_s=tok_s, ms_per_step=ms, **{k: round(v, 5) for k, v in stages.items()},
+        tokens_per_s=tok_s, ms_per_step=ms, timing=TIMING_NOTE,
+        sequential_ms_per_step=round(sum(stages.values()), 5),
+        **{k: round(v, 5) for k, v in stages.items()},
         gemm_tflops=gemm_tflops, gemm_frac_mfma=gemm_tflops / PEAK_BF16_TFLOPS,
         gemm_hbm_gbs=gemm_gbs, gemm_frac_hbm=gemm_gbs / PEAK_HBM_GBS,
         layer_bytes=work["bytes_layer"], touched_experts=work["touched"])
@@ -392,11 +429,14 @@ def main():
 
     if not args.no_extra and args.only is None:
         wl2 = Workload("prefill2048_zipf", args.copies, args.tile_m_max)
-        w2, st2 = time_workload(wl2, max(args.steps // 2, 5), max(args.warmup // 2, 3))
+        w2, st2 = time_workload(wl2, max(args.steps // 2, 5), max(args.warmup // 2, 3),
+                                overlap=args.overlap)
         wk2 = wl2.work()
         g2 = (st2["gate_up_ms"] + st2["down_ms"]) * 1e-3
         extra["prefill2048_zipf"] = dict(
-            tokens_per_s=wl2.T * max(args.steps // 2, 5) / w2, **{k: round(v, 5) for k, v in st2.items()},
+            tokens_per_s=wl2.T * max(args.steps // 2, 5) / w2, timing=TIMING_NOTE,
+            sequential_ms_per_step=round(sum(st2.values()), 5),
+            **{k: round(v, 5) for k, v in st2.items()},
             gemm_tflops=(wk2["flops_gate_up"] + wk2["flops_down"]) / g2 / 1e12,
             gemm_frac_mfma=(wk2["flops_gate_up"] + wk2["flops_down"]) / g2 / 1e12 / PEAK_BF16_TFLOPS,
             touched_experts=wk2["touched"])
