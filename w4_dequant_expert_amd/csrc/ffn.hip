@@ -25,7 +25,10 @@
 // accumulators over rebuilt bf16 weights: matrix-unit-bound work) and a
 // short-batch kernel for at most 16 tokens.  The small and tall kernels each
 // skip the blocks the other owns, so the host launches both without knowing
-// the routing.
+// the routing (for large batches, where nearly every row is in a tall block,
+// only the tall kernel, which then takes the short blocks too).  A launch
+// covers every block, only the routed ones, or only the shared expert's
+// (whose blocks follow from T alone, so that launch reads no routing tables).
 //
 // MFMA operand convention: for the 16x16x32 bf16 MFMA, lane l supplies row
 // (l mod 16) of A and column (l mod 16) of B with eight consecutive reduction
@@ -643,10 +646,7 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
   }
 }
 
-#ifndef MOE_T4CT
-#define MOE_T4CT 2
-#endif
-constexpr int kT4CT = MOE_T4CT;  // 32-column tiles per wave of the four-wave kernel
+constexpr int kT4CT = 2;  // 32-column tiles per wave of the tall-tile kernel
 
 template <bool GATE_UP>
 __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* __restrict__ src,
