@@ -52,7 +52,8 @@ def parse():
                    help="run the shared expert's FFN on a second stream, concurrent with routing")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration)")
-    p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1", "chunked16384"],
+    p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1", "chunked16384",
+                                      "small_batches", "ablations"],
                    default=None,
                    help="time a single workload (profiling runs)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -267,6 +268,111 @@ def decode_leg(copies=40):
     return out
 
 
+def small_batch_leg(Ts=(2, 4, 8), copies=40):
+    """Batches of 2..8 tokens (speculative-verification sized): whole layer
+    calls replayed from a HIP graph, a fresh batch and weight copy per call;
+    distinct experts touched and the weight bytes they pull in."""
+    import numpy as np
+    import torch
+
+    from synth import make_tokens
+    out = {}
+    for T in Ts:
+        wl = Workload("decode1", copies, T=T)
+        fresh = [torch.from_numpy(make_tokens(T, 2048, 4, t0=T * i).view(np.int16)).to("cuda")
+                 for i in range(copies)]
+        for i in range(3):
+            wl.step(i, x=fresh[i], overlap=False)
+        step_ms = graph_ms(lambda i: wl.step(i, x=fresh[i], overlap=False), copies)
+        wl.step(0, x=fresh[0], overlap=False)
+        wk = wl.work()
+        gemm_bytes = wk["bytes_gate_up"] + wk["bytes_down"]
+        out[f"T{T}"] = dict(tokens_per_s=T / (step_ms * 1e-3), ms_per_step=round(step_ms, 5),
+                            touched_experts=wk["touched"], gemm_bytes=gemm_bytes,
+                            layer_hbm_gbs=wk["bytes_layer"] / (step_ms * 1e-3) / 1e9)
+        del wl, fresh
+        torch.cuda.empty_cache()
+    return out
+
+
+def ablation_leg(copies, steps=50):
+    """Two of the pages' ablations at 512 tokens.
+    - Unfused reconstruction: expanding every touched expert's 4-bit weights to
+      bfloat16 in memory (moe_w4_dequant over the canonical layout), which an
+      unfused path must do before its GEMMs; compared with the fused layer.
+    - Host-synchronised routing: the same layer call with the block count read
+      back to the host (a device-to-host copy and a wait) between routing and
+      the GEMMs, as a host-driven expert loop needs."""
+    import numpy as np
+    import torch
+
+    import w4_dequant_expert_amd as moe
+    wl = Workload("prefill512", copies)
+    sh, c = wl.sh, wl.c
+    L = wl.layer
+    nb_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+
+    def synced(i):
+        r, s_, wr = wl.copies[i % len(wl.copies)]
+        L.w_router = wr
+        d = L.route(wl.x)
+        nb_host.copy_(L.rt.n_blocks[:1], non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        L.ffn(d, wl.x, r, s_)
+        L.combine(d, wl.y)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+    # warm the clocks on both paths, then alternate them (fused: GPU-resident
+    # routing, the headline path; synced: the block count read back first)
+    for i in range(100):
+        wl.step(i)
+    for i in range(20):
+        synced(i)
+    fused, syn = [], []
+    for _ in range(3):
+        fused.append(timed(wl.step))
+        syn.append(timed(synced))
+    fused_ms, synced_ms = min(fused), min(syn)
+    # expansion of the touched experts' weights (every expert is touched at 512 tokens)
+    bank = c["routed"]
+    E, H, I = sh.E, sh.H, sh.I
+    canon = {k: torch.from_numpy(np.ascontiguousarray(bank[k]).view(np.uint8 if k.endswith("_q") else np.int16))
+             .to("cuda") for k in ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b")}
+    gu_out = torch.empty((E * 2 * I, H), dtype=torch.int16, device="cuda")
+    dn_out = torch.empty((E * H, I), dtype=torch.int16, device="cuda")
+
+    def expand():
+        moe.moe_w4_dequant(E * 2 * I, H, canon["gu_q"], canon["gu_s"], canon["gu_b"], gu_out)
+        moe.moe_w4_dequant(E * H, I, canon["dn_q"], canon["dn_s"], canon["dn_b"], dn_out)
+    expand()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        expand()
+    e1.record()
+    torch.cuda.synchronize()
+    expand_ms = e0.elapsed_time(e1) / 10
+    expanded = (gu_out.numel() + dn_out.numel()) * 2
+    out = dict(
+        fused_layer_ms=round(fused_ms, 5),
+        host_synced_routing_layer_ms=round(synced_ms, 5),
+        gpu_resident_routing_speedup=synced_ms / fused_ms,
+        unfused_expand_ms=round(expand_ms, 5), unfused_expanded_bytes=expanded,
+        fused_over_unfused_expand_alone=expand_ms / fused_ms,
+        note="unfused_expand_ms is only the bf16 expansion of the 256 routed experts' weights "
+             "(the GEMMs an unfused path then runs come on top of it)")
+    del wl, canon, gu_out, dn_out
+    torch.cuda.empty_cache()
+    return out
+
+
 def chunked_leg(copies, reps=3):
     """Long prompt: 16384 tokens as 8 independent layer calls of 2048 tokens
     (route, gate/up, down, combine each), timed per chunk with HIP events over
@@ -407,6 +513,12 @@ def main():
     if main_name == "chunked16384":
         print(json.dumps({"chunked16384": chunked_leg(args.copies)}))
         return
+    if main_name == "small_batches":
+        print(json.dumps({"small_batches": small_batch_leg()}))
+        return
+    if main_name == "ablations":
+        print(json.dumps({"ablations_prefill512": ablation_leg(args.copies)}))
+        return
     wl = Workload(main_name, args.copies, args.tile_m_max)
     wall, stages = time_workload(wl, args.steps, args.warmup, overlap=args.overlap)
     work = wl.work()
@@ -445,6 +557,10 @@ def main():
         extra["decode1"] = decode_leg(40)
         torch.cuda.empty_cache()
         extra["chunked16384"] = chunked_leg(args.copies)
+        torch.cuda.empty_cache()
+        extra["small_batches"] = small_batch_leg()
+        torch.cuda.empty_cache()
+        extra["ablations_prefill512"] = ablation_leg(args.copies)
         torch.cuda.empty_cache()
 
     out = {
