@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration)")
     p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1", "chunked16384",
-                                      "small_batches", "ablations"],
+                                      "small_batches", "ablations", "tile_sweep"],
                    default=None,
                    help="time a single workload (profiling runs)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -373,6 +373,21 @@ def ablation_leg(copies, steps=50):
     return out
 
 
+def tile_sweep_leg(copies, steps=100, warmup=50):
+    """The pages' tile-height ablation: whole layer calls at 512 and 2048
+    (Zipf-skewed) tokens for each bound on the block map's tile height."""
+    import torch
+    out = {}
+    for name in ("prefill512", "prefill2048_zipf"):
+        for m in (16, 32, 64, 128):
+            wl = Workload(name, copies, m)
+            wall, _ = time_workload(wl, steps, warmup)
+            out[f"{name}_M{m}"] = round(wl.T * steps / wall, 1)
+            del wl
+            torch.cuda.empty_cache()
+    return out
+
+
 def chunked_leg(copies, reps=3):
     """Long prompt: 16384 tokens as 8 independent layer calls of 2048 tokens
     (route, gate/up, down, combine each), timed per chunk with HIP events over
@@ -518,6 +533,9 @@ def main():
         return
     if main_name == "ablations":
         print(json.dumps({"ablations_prefill512": ablation_leg(args.copies)}))
+        return
+    if main_name == "tile_sweep":  # tokens/s per tile-height bound (not in the default run)
+        print(json.dumps({"tile_sweep": tile_sweep_leg(args.copies)}))
         return
     wl = Workload(main_name, args.copies, args.tile_m_max)
     wall, stages = time_workload(wl, args.steps, args.warmup, overlap=args.overlap)
