@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_W4_ABI_VERSION 1
+#define MOE_W4_ABI_VERSION 2
 
 /* Return codes. */
 #define MOE_OK 0
