@@ -220,6 +220,32 @@ def graph_ms(fn, n_inner, replays=5):
     return e0.elapsed_time(e1) / (replays * n_inner)
 
 
+def stream_ceiling(nbytes, copies=40, workgroups=(256, 512, 1024, 2048, 4096)):
+    """The streaming-read ceiling B' for nbytes per launch: moe_read_probe over
+    `copies` distinct buffers (more than the Infinity Cache holds), replayed
+    from a HIP graph like the decode steps; the best launch shape counts.  Also
+    the per-launch time of a one-workgroup probe of 16 bytes (a kernel that
+    does nothing measurable), the graph's fixed cost per kernel node."""
+    import torch
+
+    import w4_dequant_expert_amd as moe
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(max(workgroups), dtype=torch.int32, device="cuda")
+    best = None
+    per_wg = {}
+    for wg in workgroups:
+        ms = graph_ms(lambda i: moe.moe_read_probe(bufs[i], n, sink, wg), copies)
+        per_wg[wg] = round(ms * 1e3, 3)
+        if best is None or ms < best[0]:
+            best = (ms, wg)
+    empty_ms = graph_ms(lambda i: moe.moe_read_probe(bufs[i], 16, sink, 1), copies)
+    del bufs
+    return dict(bytes=n, best_us=round(best[0] * 1e3, 3), workgroups=best[1],
+                gbs=n / (best[0] * 1e-3) / 1e9, us_by_workgroups=per_wg,
+                empty_kernel_us=round(empty_ms * 1e3, 3))
+
+
 def decode_leg(copies=40):
     """Batch-1 decode: whole steps and each stage timed from HIP graph replays
     (40 steps per graph, each with its own weight copy and fresh token)."""
@@ -253,6 +279,8 @@ def decode_leg(copies=40):
     cb_ms = graph_ms(lambda i: L.combine(d, wl.y), copies)
     wk = wl.work()
     g_s = ffn_ms * 1e-3  # the grouped gate/up + down call the layer uses
+    ceiling = stream_ceiling(wk["bytes_gate_up"] + wk["bytes_down"], copies)
+    gemm_gbs = (wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9
     out = dict(
         tokens_per_s=1.0 / (step_ms * 1e-3), ms_per_step=step_ms, timing="hip graph replay",
         eager_tokens_per_s=200 / w_eager,
@@ -260,8 +288,8 @@ def decode_leg(copies=40):
         gate_up_ms=round(gu_ms, 5), down_ms=round(dn_ms, 5),
         gate_up_hbm_gbs=wk["bytes_gate_up"] / (gu_ms * 1e-3) / 1e9,
         down_hbm_gbs=wk["bytes_down"] / (dn_ms * 1e-3) / 1e9,
-        gemm_hbm_gbs=(wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9,
-        gemm_frac_hbm=(wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9 / PEAK_HBM_GBS,
+        gemm_hbm_gbs=gemm_gbs, gemm_frac_hbm=gemm_gbs / PEAK_HBM_GBS,
+        stream_ceiling=ceiling, gemm_frac_of_stream_ceiling=gemm_gbs / ceiling["gbs"],
         gemm_bytes=wk["bytes_gate_up"] + wk["bytes_down"],
         bytes_per_token=wk["bytes_layer"], weight_copies=copies)
     del wl

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_W4_ABI_VERSION 2
+#define MOE_W4_ABI_VERSION 3
 
 /* Return codes. */
 #define MOE_OK 0
@@ -257,6 +257,29 @@ int moe_combine(const moe_dims *d, const moe_route_out *r, const uint16_t *y_slo
  */
 int moe_w4_dequant(int32_t rows, int32_t K, const uint8_t *q, const uint16_t *s, const uint16_t *b,
                    uint16_t *out, void *stream);
+
+/*
+ * moe_w4_dequant_packed - expand n packed matrices (moe_w4_pack's output for
+ * `rows` x K matrices, `gate_up` as given to moe_w4_pack) back to bfloat16 in
+ * the canonical [n][rows][K] order, through the packed addressing and the
+ * reconstruction w = bf16(fma(q, s, b)) of the tall-tile GEMM kernel.
+ * Diagnostic: it checks that kernel's reconstruction bit for bit and gives the
+ * unfused comparison its bfloat16 weights.
+ *   packed (16-byte aligned) n * moe_w4_packed_bytes(rows, K) bytes;
+ *   out [n][rows][K] bfloat16 (16-byte aligned).  Same size rules as
+ *   moe_w4_pack.
+ */
+int moe_w4_dequant_packed(int32_t n, int32_t rows, int32_t K, int32_t gate_up, const uint8_t *packed,
+                          uint16_t *out, void *stream);
+
+/*
+ * moe_read_probe - measurement aid, not part of the layer: one kernel that
+ * reads `bytes` (a multiple of 16) at `src` once, in 16-byte loads spread over
+ * `workgroups` workgroups of 256 threads, and writes one folded word per
+ * workgroup to sink[workgroups].  Timing it gives the streaming-read ceiling
+ * for a weight stream of the same size through the same launch path.
+ */
+int moe_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups, void *stream);
 
 #ifdef __cplusplus
 }

@@ -152,3 +152,23 @@ def test_pack_sizes_and_validation():
     assert L.moe_w4_pack(1, 16, 64, 0, 0x1008, 0x2000, 0x3000, 0x4000, None) == -2
     assert L.moe_w4_pack(1, 16, 64, 0, 0x1000, 0x2000, 0x3000, 0x4008, None) == -2
     assert L.moe_w4_pack(0, 16, 64, 0, 0x1000, 0x2000, 0x3000, 0x4000, None) == 0
+
+
+def test_route_workspace_never_shrinks_with_T():
+    """A workspace sized for a batch bound fits every smaller batch: the bytes
+    needed are non-decreasing in T (the short-batch path's class sums included)."""
+    for E, k in ((8, 2), (256, 8), (300, 8), (1024, 4)):
+        prev = 0
+        for T in list(range(0, 70)) + [100, 511, 512, 513, 2048, 4096]:
+            n = moe.moe_route_ws_bytes(moe.make_dims(T, 256, 128, E, k, 1, 32, 16))
+            assert n >= prev, (E, T, n, prev)
+            prev = n
+
+
+def test_block_bound_covers_1024_experts_with_shared():
+    """moe_max_blocks at the largest expert count with a shared expert
+    matches the oracle's bound (1025 groups)."""
+    import oracle
+    for T in (1, 5, 64, 300):
+        d = moe.make_dims(T, 128, 64, 1024, 4, 1, 16, 16)
+        assert moe.moe_max_blocks(d) == oracle.max_blocks(T, 1024, 4, 1, 16)

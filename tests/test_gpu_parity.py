@@ -2,16 +2,20 @@
 
 Routing tables (top-k indices, histogram, offsets, scatter, block map) must
 match bit for bit, the exported float32 scores too; routing weights within
-1e-6; the layer output within a relative error of 1e-2, measured per token as
-max_i |y - y_ref| / max_i |y_ref| (the worst token counts); sampled rows of the
-two GEMM outputs (h and y_slots) are held to the same bound against the
-oracle's single-expert FFN.
+1e-6.  The layer output is held to a relative error of 1e-2 per token,
+max_i |y - y_ref| / max_i |y_ref| (the worst token counts), and its per-element
+error, |y - y_ref| / max(|y_ref|, rms of the row), to at most 5 % above that of
+a CPU model of the kernels' rounding pipeline on the same tokens
+(tests/emulate.py; why the per-token metric is the gate is pinned in
+tests/test_tolerance_reading.py).  One row of h and y_slots per block of the
+map (every block) is checked against the oracle's single-expert FFN.  Every
+output buffer carries guard bytes on both sides that must survive the call.
 """
 
 from __future__ import annotations
 
-import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -20,14 +24,18 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
+import emulate  # noqa: E402
 import oracle  # noqa: E402
 import w4_dequant_expert_amd as moe  # noqa: E402
 from synth import FULL_SHAPE, bf16_bits_to_f32, build_config, make_bank, make_router, make_tokens  # noqa: E402
 from synth.configs import _banks  # noqa: E402
 
 TOL_Y = 1e-2
+EL_SLACK = 1.05
 TOL_W = 1e-6
 NTHREADS = 16
+GUARD = 256          # guard bytes on each side of every output buffer
+GUARD_BYTE = 0x5A
 
 
 def note(msg):
@@ -46,6 +54,54 @@ def y_to_f64(y_bits):
     return bf16_bits_to_f32(np.asarray(y_bits).view(np.uint16)).astype(np.float64)
 
 
+class Guarded:
+    """Device buffers with GUARD bytes of a fixed pattern before and after each."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def __call__(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        raw = torch.full((n + 2 * GUARD,), GUARD_BYTE, dtype=torch.uint8, device="cuda")
+        self.bufs.append((raw, n))
+        return raw[GUARD:GUARD + n].view(dtype).view(shape)
+
+    def check(self, label=""):
+        torch.cuda.synchronize()
+        for raw, n in self.bufs:
+            head, tail = raw[:GUARD], raw[GUARD + n:]
+            assert bool((head == GUARD_BYTE).all()) and bool((tail == GUARD_BYTE).all()), \
+                f"{label}: a kernel wrote outside an output buffer"
+
+
+def guard_layer(layer, T):
+    """Point every output of the layer at guarded buffers (the tables, h, y_slots)."""
+    g = Guarded()
+    rt = layer.rt
+    d = rt.d
+    rows = d.T * d.k + (d.T if d.n_shared else 0)
+    rt.topk_idx = g((d.T, d.k), torch.int32)
+    rt.topk_w = g((d.T, d.k), torch.float32)
+    rt.counts = g((d.E,), torch.int32)
+    rt.offsets = g((d.E + 1,), torch.int32)
+    rt.sorted_slot = g((d.T * d.k,), torch.int32)
+    rt.slot_pos = g((d.T * d.k,), torch.int32)
+    rt.blocks = g((max(rt.max_blocks, 1), 4), torch.int32)
+    rt.n_blocks = g((1,), torch.int32)
+    if rt.logits is not None:
+        rt.logits = g((d.T, d.E), torch.float32)
+    rt.status = g((1,), torch.int32)
+    rt.c = moe.RouteOut(rt.topk_idx.data_ptr(), rt.topk_w.data_ptr(), rt.counts.data_ptr(),
+                        rt.offsets.data_ptr(), rt.sorted_slot.data_ptr(), rt.slot_pos.data_ptr(),
+                        rt.blocks.data_ptr(), rt.n_blocks.data_ptr(),
+                        rt.logits.data_ptr() if rt.logits is not None else None,
+                        rt.status.data_ptr(), rt.ws.data_ptr(), rt.ws_bytes)
+    layer.h = g((rows, layer.I), torch.int16)
+    layer.y_slots = g((rows, layer.H), torch.int16)
+    y = g((T, layer.H), torch.int16)
+    return g, y
+
+
 @pytest.fixture(scope="module")
 def full_banks():
     routed, shared = _banks(FULL_SHAPE, 1)
@@ -53,78 +109,132 @@ def full_banks():
 
 
 def run_layer(x, wr, bias, routed_np, shared_np, routed_dev, shared_dev, k, tile_m_max=128,
-              tile_gran=16, n_shared=1):
+              tile_gran=16, n_shared=1, T_max=None):
+    """One layer call through the C ABI into guarded buffers; returns the layer,
+    its routing tables on the host and y (bf16 bits)."""
     T, H = x.shape
     E = wr.shape[1]
     I = routed_np["gu_q"].shape[1] // 2
     layer = moe.MoeLayer(H, I, E, k, n_shared, routed_dev, shared_dev if n_shared else None, wr,
-                         bias, T_max=max(T, 1), tile_m_max=tile_m_max, tile_gran=tile_gran,
-                         export_logits=True)
+                         bias, T_max=T_max or max(T, 1), tile_m_max=tile_m_max,
+                         tile_gran=tile_gran, export_logits=True)
+    guards, y = guard_layer(layer, T)
     xd = dev(x)
-    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     layer.forward(xd, y)
     torch.cuda.synchronize()
+    guards.check(f"T={T} E={E}")
     return layer, layer.rt.host(), y.cpu().numpy()
 
 
 def check_routing(g, r, label=""):
     assert g["status"] == 0, f"{label} status {g['status']}"
-    assert np.array_equal(g["logits"].view(np.uint32), r["logits"].view(np.uint32)), label
-    assert np.array_equal(g["topk_idx"], r["topk_idx"]), label
+    T = r["topk_idx"].shape[0]
+    assert np.array_equal(g["logits"][:T].view(np.uint32), r["logits"].view(np.uint32)), label
+    assert np.array_equal(g["topk_idx"][:T], r["topk_idx"]), label
     assert np.array_equal(g["counts"], r["counts"]), label
     assert np.array_equal(g["offsets"], r["offsets"]), label
-    assert np.array_equal(g["sorted_slot"], r["sorted_slot"]), label
-    assert np.array_equal(g["slot_pos"], r["slot_pos"]), label
+    Sk = r["sorted_slot"].shape[0]
+    assert np.array_equal(g["sorted_slot"][:Sk], r["sorted_slot"]), label
+    assert np.array_equal(g["slot_pos"][:Sk], r["slot_pos"]), label
     assert g["n_blocks"] == len(r["blocks"]), label
     assert np.array_equal(g["blocks"], r["blocks"]), label
-    assert np.max(np.abs(g["topk_w"] - r["topk_w"])) <= TOL_W, label
+    assert np.max(np.abs(g["topk_w"][:T] - r["topk_w"])) <= TOL_W, label
 
 
-def check_intermediates(layer, g, x, routed_np, shared_np, k, nrows=6, seed=0):
-    """Sampled rows of h (gate/up output) and y_slots (down output) against the
-    oracle's single-expert FFN: each GEMM is checked on its own."""
-    T = x.shape[0]
+def block_rows(blocks, extra=()):
+    """One row of every block of the map (a pseudo-random row inside it), plus extra rows."""
+    rows = set(int(r) for r in extra)
+    for b, (grp, r0, n, tm) in enumerate(np.asarray(blocks).reshape(-1, 4).tolist()):
+        rows.add(r0 + (b * 7919 + 13) % n)
+    return sorted(rows)
+
+
+def check_intermediates(layer, g, x, routed_np, shared_np, k, T, tile_m_max, label=""):
+    """One row of h (gate/up output) and of y_slots (down output) per block of
+    the map against the oracle's single-expert FFN: each GEMM, each block.  A
+    row passes within 1e-2 per row (normwise), or within 5 % above the error
+    the rounding model makes on that row (short rows of small layers round
+    more than the 1e-2 the whole layer is held to)."""
     Sk = T * k
+    E = routed_np["gu_q"].shape[0]
     rows_total = Sk + (T if shared_np is not None else 0)
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, rows_total - 1], rng.choice(rows_total, min(nrows, rows_total), replace=False)]))
+    rows = block_rows(g["blocks"], (0, rows_total - 1))
     h = layer.h.cpu().numpy().view(np.uint16)
     ys = layer.y_slots.cpu().numpy().view(np.uint16)
+    want = []
     for r in rows:
         if r < Sk:
             slot = int(g["sorted_slot"][r])
-            t, e, bank = slot // k, int(g["topk_idx"][slot // k, slot % k]), routed_np
+            want.append((r, slot // k, int(g["topk_idx"][slot // k, slot % k])))
         else:
-            t, e, bank = int(r - Sk), 0, shared_np
-        h_ref, y_ref = oracle.expert_ffn(x[t], bank, e)
-        eh = oracle.relative_error(bf16_bits_to_f32(h[r]).astype(np.float64), h_ref)
-        ey = oracle.relative_error(bf16_bits_to_f32(ys[r]).astype(np.float64), y_ref)
-        assert eh <= TOL_Y and ey <= TOL_Y, (r, eh, ey)
+            want.append((r, int(r - Sk), E))
+    forms = emulate.row_weight_forms(T, k, E, rows_total, tile_m_max, g["blocks"])
+    h_em, ys_em = emulate.expert_rows(bf16_bits_to_f32(x).astype(np.float64), want, forms,
+                                      routed_np, shared_np)
+
+    def one(item):
+        r, t, e = item
+        bank, ee = (routed_np, e) if e < E else (shared_np, 0)
+        h_ref, y_ref = oracle.expert_ffn(x[t], bank, ee)
+        hg = bf16_bits_to_f32(h[r]).astype(np.float64)
+        yg = bf16_bits_to_f32(ys[r]).astype(np.float64)
+        return (r, oracle.relative_error(hg, h_ref), oracle.relative_error(h_em[r], h_ref),
+                oracle.relative_error(yg, y_ref), oracle.relative_error(ys_em[r], y_ref),
+                oracle.relative_error(hg, h_em[r]), oracle.relative_error(yg, ys_em[r]))
+
+    with ThreadPoolExecutor(NTHREADS) as pool:   # ctypes releases the GIL in the oracle
+        res = list(pool.map(one, want))
+    worst = max(res, key=lambda v: max(v[1], v[3]))
+    note(f"  intermediates: {len(rows)} rows over {len(g['blocks'])} blocks; worst row {worst[0]}: "
+         f"h {worst[1]:.3e} (model {worst[2]:.3e}), y_slots {worst[3]:.3e} (model {worst[4]:.3e}); "
+         f"GPU vs model at most h {max(v[5] for v in res):.3e}, y_slots {max(v[6] for v in res):.3e}")
+    for r, eh, eh_m, ey, ey_m, _, _ in res:
+        assert eh <= max(TOL_Y, EL_SLACK * eh_m), (label, r, "h", eh, eh_m)
+        assert ey <= max(TOL_Y, EL_SLACK * ey_m), (label, r, "y_slots", ey, ey_m)
+
+
+def check_output(x, r, y, routed_np, shared_np, tile_m_max, toks, label=""):
+    """y on the listed tokens against the oracle: per token within 1e-2, and per
+    element within 5 % of the emulated rounding pipeline's error."""
+    yref = oracle.moe_layer(x, r["topk_idx"], r["topk_w"], routed_np, shared_np, tokens=toks,
+                            nthreads=NTHREADS)
+    ygpu = y_to_f64(y[toks])
+    yem, _, _ = emulate.layer(x, r, routed_np, shared_np, tile_m_max, tokens=toks)
+    err = oracle.relative_error(ygpu, yref)
+    el = oracle.relative_error_elementwise(ygpu, yref)
+    err_em = oracle.relative_error(yem, yref)
+    el_em = oracle.relative_error_elementwise(yem, yref)
+    d_em = oracle.relative_error_elementwise(ygpu, yem)
+    rms = np.sqrt(np.mean(yem * yem, axis=1, keepdims=True))
+    dd = np.abs(ygpu - yem) / np.maximum(np.maximum(np.abs(yem), rms), 1e-30)
+    ti, ci = np.unravel_index(int(np.argmax(dd)), dd.shape)
+    note(f"  {label}: per token {err:.3e} (model {err_em:.3e}), per element {el:.3e} "
+         f"(model {el_em:.3e}), GPU vs model per element {d_em:.3e} at token {toks[ti]} col {ci} "
+         f"(gpu {ygpu[ti, ci]:.6g} model {yem[ti, ci]:.6g} oracle {yref[ti, ci]:.6g} "
+         f"rms {rms[ti, 0]:.4g}), {len(toks)} tokens")
+    assert err <= TOL_Y, (label, err)
+    assert el <= EL_SLACK * el_em, (label, el, el_em)
+    return err, el
 
 
 def check_layer(cfg, T=None, t0=0, tile_m_max=128, sample=None, banks=None, label=""):
     c = build_config(cfg, T=T, t0=t0, with_weights=False)
     sh = c["shape"]
     routed_np, shared_np, routed_dev, shared_dev = banks
-    note(f"case {label or cfg}: T={c['T']} t0={t0} tile_m_max={tile_m_max}")
+    label = label or cfg
+    note(f"case {label}: T={c['T']} t0={t0} tile_m_max={tile_m_max}")
     layer, g, y = run_layer(c["x"], c["wr"], c["bias"], routed_np, shared_np, routed_dev,
                             shared_dev, sh.k, tile_m_max)
     r = oracle.route(c["x"], c["wr"], c["bias"], sh.k, sh.n_shared, tile_m_max, 16, NTHREADS)
-    check_routing(g, r, label or cfg)
+    check_routing(g, r, label)
     Tn = c["T"]
     if sample is None or sample >= Tn:
         toks = np.arange(Tn)
     else:
         rng = np.random.default_rng(Tn + t0)
         toks = np.unique(np.concatenate([[0, Tn - 1], rng.choice(Tn, sample - 2, replace=False)]))
-    yref = oracle.moe_layer(c["x"], r["topk_idx"], r["topk_w"], routed_np, shared_np,
-                            tokens=toks, nthreads=NTHREADS)
-    err = oracle.relative_error(y_to_f64(y[toks]), yref)
-    err_el = oracle.relative_error_elementwise(y_to_f64(y[toks]), yref)
-    note(f"  rel err {err:.3e} (elementwise/rms-floor {err_el:.3e}) over {len(toks)} tokens, "
-         f"blocks {g['n_blocks']}")
-    assert err <= TOL_Y
-    check_intermediates(layer, g, c["x"], routed_np, shared_np, sh.k, seed=Tn + t0)
+    check_output(c["x"], r, y, routed_np, shared_np, tile_m_max, toks, label)
+    check_intermediates(layer, g, c["x"], routed_np, shared_np, sh.k, Tn, tile_m_max, label)
     return layer, g, y
 
 
@@ -142,6 +252,44 @@ def test_dequant_bit_exact(full_banks):
         ref = oracle.dequant(routed_np[f"{part}_q"][3], routed_np[f"{part}_s"][3],
                              routed_np[f"{part}_b"][3])
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_packed_bit_exact(full_banks):
+    """The tall-tile GEMM's own reconstruction (its packed addressing and
+    dequant8_pairs) on the packed weights the layer runs with: bit for bit
+    the oracle's bf16(fma(q, s, b))."""
+    routed_np, _, routed_dev, _ = full_banks
+    note("case packed dequant experts 0, 3, 255")
+    for e in (0, 3, 255):
+        for part, rows, K, gate_up in (("gu", 1024, 2048, True), ("dn", 2048, 512, False)):
+            out = torch.empty((rows, K), dtype=torch.int16, device="cuda")
+            moe.moe_w4_dequant_packed(1, rows, K, gate_up, routed_dev.t[part][e], out)
+            torch.cuda.synchronize()
+            got = bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
+            ref = oracle.dequant(routed_np[f"{part}_q"][e], routed_np[f"{part}_s"][e],
+                                 routed_np[f"{part}_b"][e])
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (e, part)
+
+
+@pytest.mark.parametrize("N,K,gate_up", [(64, 256, True), (32, 192, False), (48, 64, False)])
+def test_dequant_packed_general(N, K, gate_up):
+    """Any codes, scales and biases (signs, wide exponents, K tails), through
+    moe_w4_pack and back through the tall kernel's reconstruction."""
+    note(f"case packed dequant general N={N} K={K} gate_up={gate_up}")
+    from synth import f64_to_bf16_bits
+    rng = np.random.default_rng(N * K)
+    q = rng.integers(0, 256, (2, N, K // 2), dtype=np.uint8)
+    mag = lambda: rng.uniform(-3, 3, (2, N, K // 64)) * np.exp(rng.uniform(-30, 30, (2, N, K // 64)))
+    s_, b = f64_to_bf16_bits(mag()), f64_to_bf16_bits(mag())
+    packed = torch.zeros((2, moe.moe_w4_packed_bytes(N, K)), dtype=torch.uint8, device="cuda")
+    moe.moe_w4_pack(2, N, K, gate_up, dev(q), dev(s_), dev(b), packed)
+    out = torch.empty((2, N, K), dtype=torch.int16, device="cuda")
+    moe.moe_w4_dequant_packed(2, N, K, gate_up, packed, out)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
+    for e in range(2):
+        ref = oracle.dequant(q[e], s_[e], b[e])
+        assert np.array_equal(got[e].view(np.uint32), ref.view(np.uint32)), e
 
 
 def unpack_host(packed, N, K, gate_up):
@@ -224,7 +372,7 @@ def test_tiny_layer_full_parity():
     check_layer("tiny16", banks=(c["routed"], c["shared"], rd, sd))
 
 
-@pytest.mark.parametrize("tile_m_max", [16, 32, 64])
+@pytest.mark.parametrize("tile_m_max", [16, 32, 64, 128])
 def test_tiny_layer_tiles(tile_m_max):
     c = build_config("tiny16", T=150)
     rd, sd = moe.DeviceBank(c["routed"]), moe.DeviceBank(c["shared"])
@@ -234,32 +382,123 @@ def test_tiny_layer_tiles(tile_m_max):
 
 # ----------------------------------------------------------------------------- full shape
 
-@pytest.mark.parametrize("T", [1, 37, 300])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 37, 300])
 def test_full_shape_reduced_T_all_tokens(full_banks, T):
-    sample = None if T <= 64 else 48
-    check_layer("prefill512", T=T, banks=full_banks, sample=sample, label=f"full T={T}")
+    """Small batches (the 2..8-token verification sizes among them) and two
+    mid-sized ones, every token."""
+    check_layer("decode1", T=T, t0=100, banks=full_banks, tile_m_max=32, label=f"full T={T}")
 
 
-def test_prefill512(full_banks):
-    check_layer("prefill512", banks=full_banks, sample=24)
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("tile_m_max", [32, 128])
+def test_prefill512_all_tokens(full_banks, tile_m_max):
+    """The 512-token prefill workload, every token; 32 is the tile bound the
+    benchmark runs it with."""
+    check_layer("prefill512", tile_m_max=tile_m_max, banks=full_banks, label=f"prefill512 M={tile_m_max}")
 
 
-def test_prefill2048_zipf(full_banks):
-    _, g, _ = check_layer("prefill2048_zipf", banks=full_banks, sample=24)
+@pytest.mark.timeout(300)
+def test_prefill2048_zipf_all_tokens(full_banks):
+    """The skewed 2048-token workload at the benchmark's tile bound, every token."""
+    _, g, _ = check_layer("prefill2048_zipf", banks=full_banks)
     counts = g["counts"]
     assert (counts == 0).sum() >= 1 and (counts > 200).sum() >= 1
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("tile_m_max", [32, 64])
 def test_prefill2048_zipf_tiles(full_banks, tile_m_max):
-    check_layer("prefill2048_zipf", tile_m_max=tile_m_max, banks=full_banks, sample=12,
+    check_layer("prefill2048_zipf", tile_m_max=tile_m_max, banks=full_banks, sample=160,
                 label=f"zipf M={tile_m_max}")
 
 
-@pytest.mark.parametrize("chunk", [0, 7])
+@pytest.mark.timeout(300)
+def test_chunked16384_routing_every_chunk(full_banks):
+    """Routing of all eight 2048-token chunks of the long prompt, bit for bit."""
+    routed_np, shared_np, rd, sd = full_banks
+    c0 = build_config("chunked16384", T=2048, with_weights=False)
+    sh = c0["shape"]
+    layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, rd, sd, c0["wr"], None, T_max=2048,
+                         tile_m_max=128, export_logits=True)
+    for ch in range(8):
+        note(f"case chunk {ch} routing")
+        c = build_config("chunked16384", T=2048, t0=2048 * ch, with_weights=False)
+        layer.route(dev(c["x"]))
+        torch.cuda.synchronize()
+        r = oracle.route(c["x"], c["wr"], None, sh.k, sh.n_shared, 128, 16, NTHREADS)
+        check_routing(layer.rt.host(), r, f"chunk {ch}")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("chunk", [0, 3, 7])
 def test_chunked16384_chunks(full_banks, chunk):
-    check_layer("chunked16384", T=2048, t0=2048 * chunk, banks=full_banks, sample=12,
+    check_layer("chunked16384", T=2048, t0=2048 * chunk, banks=full_banks, sample=160,
                 label=f"chunk {chunk}")
+
+
+@pytest.mark.timeout(300)
+def test_decode1_every_token(full_banks):
+    """The 1000 batch-1 decode steps, each its own layer call: routing bit for
+    bit and the output of every token."""
+    routed_np, shared_np, rd, sd = full_banks
+    c = build_config("decode1", T=1000, with_weights=False)
+    sh = c["shape"]
+    layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, rd, sd, c["wr"], None, T_max=1,
+                         tile_m_max=32, export_logits=True)
+    guards, y1 = guard_layer(layer, 1)
+    xd = dev(c["x"])
+    note("case decode1: 1000 steps")
+    ys, tabs = [], []
+    for i in range(1000):
+        layer.forward(xd[i:i + 1], y1)
+        tabs.append((layer.rt.logits.clone(), layer.rt.topk_idx.clone(), layer.rt.topk_w.clone(),
+                     layer.rt.blocks.clone(), layer.rt.status.clone()))
+        ys.append(y1.clone())
+    torch.cuda.synchronize()
+    guards.check("decode1")
+    r = oracle.route(c["x"], c["wr"], None, sh.k, sh.n_shared, 32, 16, NTHREADS)
+    logits = torch.cat([t[0] for t in tabs]).cpu().numpy()
+    idx = torch.cat([t[1] for t in tabs]).cpu().numpy()
+    w = torch.cat([t[2] for t in tabs]).cpu().numpy()
+    status = torch.cat([t[4] for t in tabs]).cpu().numpy()
+    assert np.all(status == 0)
+    assert np.array_equal(logits.view(np.uint32), r["logits"].view(np.uint32))
+    assert np.array_equal(idx, r["topk_idx"])
+    assert np.max(np.abs(w - r["topk_w"])) <= TOL_W
+    # every step's block map: its 8 experts in ascending order, one row each, then the shared one
+    for i in (0, 1, 500, 999):
+        bl = tabs[i][3][:9].cpu().numpy()
+        exp = sorted(r["topk_idx"][i].tolist())
+        assert bl.tolist() == [[e, j, 1, 16] for j, e in enumerate(exp)] + [[256, 8, 1, 16]]
+    y = torch.cat(ys).cpu().numpy()
+    # the oracle evaluates each token on its own, so one batch of 1000 is the same
+    # as 1000 one-token batches
+    yref = oracle.moe_layer(c["x"], r["topk_idx"], r["topk_w"], routed_np, shared_np,
+                            nthreads=NTHREADS)
+    ygpu = y_to_f64(y)
+    # one-token batches run the short-batch kernels, which scale after the
+    # product: every row of the model takes the exact affine weights
+    yem = emulate.layer(c["x"], r, routed_np, shared_np, 32, exact=True)[0]
+    err, el = oracle.relative_error(ygpu, yref), oracle.relative_error_elementwise(ygpu, yref)
+    el_em = oracle.relative_error_elementwise(yem, yref)
+    note(f"  decode1: per token {err:.3e}, per element {el:.3e} (model {el_em:.3e}), "
+         f"GPU vs model {oracle.relative_error_elementwise(ygpu, yem):.3e}")
+    assert err <= TOL_Y and el <= EL_SLACK * el_em
+
+
+def test_short_batches_in_a_larger_layer(full_banks):
+    """Batches of 8 and 20 tokens through a layer sized for 64: the workspace
+    sized for the bound serves the short-batch path too."""
+    routed_np, shared_np, rd, sd = full_banks
+    for T in (8, 20):
+        c = build_config("decode1", T=T, t0=300, with_weights=False)
+        sh = c["shape"]
+        note(f"case T={T} in a layer of T_max=64")
+        layer, g, y = run_layer(c["x"], c["wr"], None, routed_np, shared_np, rd, sd, sh.k,
+                                tile_m_max=32, T_max=64)
+        r = oracle.route(c["x"], c["wr"], None, sh.k, sh.n_shared, 32, 16, NTHREADS)
+        check_routing(g, r, f"T={T} of 64")
+        check_output(c["x"], r, y, routed_np, shared_np, 32, np.arange(T), f"T={T} of 64")
 
 
 @pytest.mark.parametrize("T", [1, 5, 16, 48])
@@ -333,11 +572,6 @@ def test_split_ffn_matches_grouped(full_banks, cfg, T, tile_m_max):
         assert torch.equal(layer.y_slots, ys_ref), rep
 
 
-@pytest.mark.parametrize("tok", [0, 1, 999])
-def test_decode1_tokens(full_banks, tok):
-    check_layer("decode1", T=1, t0=tok, banks=full_banks, label=f"decode token {tok}")
-
-
 def test_deterministic_and_chunk_independent(full_banks):
     routed_np, shared_np, rd, sd = full_banks
     c = build_config("chunked16384", T=4096, with_weights=False)
@@ -382,6 +616,12 @@ def test_routing_batch_sizes(full_banks, T):
     (2112, 64, 16, 2, 1, 3, 32),    # short batch: a wave with more steps than one load chunk
     (192, 64, 5, 5, 1, 200, 128),   # tall tiles (every expert 200 rows: blocks of 100) with K tails
     (1088, 320, 24, 4, 1, 300, 128),  # tall and small tiles, K tails in both GEMMs
+    (256, 128, 300, 8, 1, 5, 32),   # more than 256 experts, short batch: one-kernel scores, wide top-k
+    (256, 128, 300, 8, 1, 64, 32),  # more than 256 experts: tiled scores, wide top-k, scan
+    (128, 64, 1024, 4, 1, 5, 16),   # 1024 experts and a shared one: 1025 groups in the block map
+    (128, 64, 1024, 4, 1, 64, 16),
+    (128, 64, 1024, 8, 1, 600, 32),  # 1025 groups, several rows per expert
+    (128, 64, 1024, 4, 0, 64, 16),  # 1024 experts, no shared expert
 ])
 def test_odd_shapes(H, I, E, k, n_shared, T, tile_m_max):
     note(f"case odd shape H={H} I={I} E={E} k={k} shared={n_shared} T={T} tile {tile_m_max}")
@@ -391,12 +631,12 @@ def test_odd_shapes(H, I, E, k, n_shared, T, tile_m_max):
     x = make_tokens(T, H, seed=21)
     rd = moe.DeviceBank(routed)
     sd = moe.DeviceBank(shared) if n_shared else None
-    _, g, y = run_layer(x, wr, None, routed, shared, rd, sd, k, tile_m_max=tile_m_max,
-                        n_shared=n_shared)
+    layer, g, y = run_layer(x, wr, None, routed, shared, rd, sd, k, tile_m_max=tile_m_max,
+                            n_shared=n_shared)
     r = oracle.route(x, wr, None, k, n_shared, tile_m_max, 16, NTHREADS)
     check_routing(g, r)
-    yref = oracle.moe_layer(x, r["topk_idx"], r["topk_w"], routed, shared, nthreads=NTHREADS)
-    assert oracle.relative_error(y_to_f64(y), yref) <= TOL_Y
+    check_output(x, r, y, routed, shared, tile_m_max, np.arange(T), f"H={H} I={I} E={E} T={T}")
+    check_intermediates(layer, g, x, routed, shared, k, T, tile_m_max, f"E={E} T={T}")
 
 
 def test_nan_input_sets_status_and_keeps_indices_in_range():

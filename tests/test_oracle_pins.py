@@ -418,3 +418,33 @@ def test_zipf_config_reading(orc):
 def test_router_init_scale():
     wr = make_router(2048, 256, 0.02, seed=1)
     assert abs(wr.std() - 0.02) < 2e-4 and abs(wr.mean()) < 2e-4
+
+
+# ---------------------------------------------------------------- the output metrics
+
+def test_relative_error_metrics_hand_computed(orc):
+    """Both layer-output metrics on arrays worked out by hand: a zero reference
+    row (its denominator falls back to 1), and a worst token that is not the
+    first one."""
+    y_ref = np.array([[1.0, -2.0, 0.5],
+                      [0.0, 0.0, 0.0],
+                      [4.0, 1.0, -1.0]])
+    delta = np.array([[0.01, 0.0, 0.0],
+                      [0.001, 0.0, 0.0],
+                      [0.0, 0.1, 0.0]])
+    y = y_ref + delta
+    # normwise, per token max_i |dy| / max_i |y_ref|: 0.01/2, 0.001/1, 0.1/4
+    assert orc.relative_error(y, y_ref) == pytest.approx(0.025, rel=1e-12)
+    assert orc.relative_error(y[:2], y_ref[:2]) == pytest.approx(0.005, rel=1e-12)
+    # elementwise, |dy| / max(|y_ref|, rms of the token's row):
+    # row 0: 0.01 / max(1, sqrt(5.25/3)); row 1: 0.001 / 1; row 2: 0.1 / max(1, sqrt(18/3))
+    assert orc.relative_error_elementwise(y, y_ref) == pytest.approx(0.1 / math.sqrt(6.0), rel=1e-12)
+    assert orc.relative_error_elementwise(y[:1], y_ref[:1]) == pytest.approx(0.01 / math.sqrt(1.75),
+                                                                            rel=1e-12)
+    # an element larger than its row's rms is measured against itself
+    assert orc.relative_error_elementwise(np.array([[10.5, 0.0, 0.0, 0.0]]),
+                                          np.array([[10.0, 0.0, 0.0, 0.0]])) == pytest.approx(0.05)
+    # symmetric in the sign of the error, exact on equality, empty is zero
+    assert orc.relative_error(y_ref - delta, y_ref) == pytest.approx(0.025, rel=1e-12)
+    assert orc.relative_error(y_ref, y_ref) == 0.0 == orc.relative_error_elementwise(y_ref, y_ref)
+    assert orc.relative_error(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0

@@ -27,7 +27,9 @@ from .moe import (  # noqa: F401
     moe_route_ws_bytes,
     moe_routed_w4_ffn,
     moe_shared_w4_ffn,
+    moe_read_probe,
     moe_w4_dequant,
+    moe_w4_dequant_packed,
     moe_w4_pack,
     moe_w4_packed_bytes,
     moe_w4_down,

@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "route.h"
@@ -60,8 +61,12 @@ WsLayout ws_layout(const moe_dims& d, bool need_logits) {
   off += align256(W * E * 4);
   L.pref = off;
   off += align256(W * E * 4);
-  L.part = off;  // router class sums of the short-batch path
-  off += (T <= 16 && E <= 256) ? align256(8 * T * E * 4) : 0;
+  // Router class sums of the short-batch path (T <= 16, E <= 256).  The
+  // region is sized for min(T, 16) tokens at every T, so that the total never
+  // decreases with T: a workspace sized for a batch bound fits every smaller
+  // batch, including the short ones that use this region.
+  L.part = off;
+  off += (E <= 256) ? align256(8 * std::min<size_t>(T, 16) * E * 4) : 0;
   L.total = off;
   return L;
 }
@@ -139,6 +144,41 @@ GemmArgs gemm_args(const moe_dims& d, const moe_route_out* r, const moe_w4_bank*
 
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
+int validate_route_args(const moe_dims* d, const uint16_t* x, const float* w_router,
+                        const float* logit_bias, const moe_route_out* out, bool need_ws) {
+  int rc = validate_dims(d);
+  if (rc) return rc;
+  if ((rc = validate_route_out(out, need_ws))) return rc;
+  if (!x || !w_router) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 4) || (logit_bias && !aligned(logit_bias, 4)))
+    return MOE_EALIGN;
+  return MOE_OK;
+}
+
+// Routing with its scratch at ws (layout L): the kernels clear what they
+// accumulate into (the token bitmask) themselves.
+int enqueue_route(const moe_dims& d, const uint16_t* x, const float* w_router,
+                  const float* logit_bias, const moe_route_out* out, char* ws, const WsLayout& L,
+                  hipStream_t stream) {
+  RouteBuffers rb{};
+  rb.logits = out->logits ? out->logits : reinterpret_cast<float*>(ws + L.logits);
+  rb.topk_idx = out->topk_idx;
+  rb.topk_w = out->topk_w;
+  rb.counts = out->counts;
+  rb.offsets = out->offsets;
+  rb.sorted_slot = out->sorted_slot;
+  rb.slot_pos = out->slot_pos;
+  rb.blocks = out->blocks;
+  rb.n_blocks = out->n_blocks;
+  rb.bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+  rb.pref = reinterpret_cast<int32_t*>(ws + L.pref);
+  rb.part = reinterpret_cast<float*>(ws + L.part);
+  rb.status = out->status;
+  rb.max_blocks = max_blocks_of(d);
+  (void)hipGetLastError();
+  return launched(launch_route(d, x, w_router, logit_bias, rb, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,34 +209,14 @@ size_t moe_route_ws_bytes(const moe_dims* d) {
 
 int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const float* logit_bias,
               const moe_route_out* out, void* stream) {
-  int rc = validate_dims(d);
+  int rc = validate_route_args(d, x, w_router, logit_bias, out, true);
   if (rc) return rc;
-  if ((rc = validate_route_out(out, true))) return rc;
-  if (!x || !w_router) return MOE_EINVAL;
-  if (!aligned(x, 16) || !aligned(w_router, 4) || (logit_bias && !aligned(logit_bias, 4)))
-    return MOE_EALIGN;
   const WsLayout L = ws_layout(*d, out->logits == nullptr);
   if (out->ws_bytes < L.total) return MOE_EWS;
   if (d->T == 0) return MOE_OK;
   if ((rc = check_device())) return rc;
-  char* ws = static_cast<char*>(out->ws);
-  RouteBuffers rb{};
-  rb.logits = out->logits ? out->logits : reinterpret_cast<float*>(ws + L.logits);
-  rb.topk_idx = out->topk_idx;
-  rb.topk_w = out->topk_w;
-  rb.counts = out->counts;
-  rb.offsets = out->offsets;
-  rb.sorted_slot = out->sorted_slot;
-  rb.slot_pos = out->slot_pos;
-  rb.blocks = out->blocks;
-  rb.n_blocks = out->n_blocks;
-  rb.bits = reinterpret_cast<uint32_t*>(ws + L.bits);
-  rb.pref = reinterpret_cast<int32_t*>(ws + L.pref);
-  rb.part = reinterpret_cast<float*>(ws + L.part);
-  rb.status = out->status;
-  rb.max_blocks = max_blocks_of(*d);
-  (void)hipGetLastError();
-  return launched(launch_route(*d, x, w_router, logit_bias, rb, static_cast<hipStream_t>(stream)));
+  return enqueue_route(*d, x, w_router, logit_bias, out, static_cast<char*>(out->ws), L,
+                       static_cast<hipStream_t>(stream));
 }
 
 int moe_w4_gate_up(const moe_dims* d, const uint16_t* x, const moe_route_out* r,
@@ -335,6 +355,29 @@ int moe_w4_dequant(int32_t rows, int32_t K, const uint8_t* q, const uint16_t* s,
   if (rc) return rc;
   (void)hipGetLastError();
   return launched(launch_dequant(rows, K, q, s, b, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_w4_dequant_packed(int32_t n, int32_t rows, int32_t K, int32_t gate_up, const uint8_t* packed,
+                          uint16_t* out, void* stream) {
+  if (n < 0 || !pack_dims_ok(rows, K) || (gate_up != 0 && gate_up != 1)) return MOE_EINVAL;
+  if (!packed || !out) return MOE_EINVAL;
+  if (!aligned(packed, 16) || !aligned(out, 16)) return MOE_EALIGN;
+  if (n == 0) return MOE_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return launched(launch_dequant_packed(n, rows, K, gate_up, packed, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!src || !sink || workgroups < 1 || workgroups > (1 << 20)) return MOE_EINVAL;
+  if (!aligned(src, 16) || bytes % 16 || !aligned(sink, 4)) return MOE_EALIGN;
+  if (bytes == 0) return MOE_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return launched(launch_read_probe(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

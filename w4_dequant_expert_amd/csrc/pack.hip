@@ -95,4 +95,45 @@ hipError_t launch_dequant(int rows, int K, const uint8_t* q, const uint16_t* s, 
   return hipGetLastError();
 }
 
+
+// Diagnostic expansion of packed matrices back to the canonical [rows][K]
+// order, through the packed addressing and the reconstruction the tall-tile
+// GEMM uses (dequant8_pairs on one packed code word and its group's scale and
+// bias).  One thread per (matrix, slice, step, lane, word): eight weights.
+__global__ __launch_bounds__(256) void dequant_packed_kernel(int nmat, int N, int K, int gate_up,
+                                                             const uint8_t* __restrict__ packed,
+                                                             uint16_t* __restrict__ out) {
+  const int nk = pack_steps(K);
+  const int nsl = N / 16;
+  const long long total = static_cast<long long>(nmat) * nsl * nk * 64 * 4;
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int j = static_cast<int>(idx % 4);
+  long long rest = idx / 4;
+  const int lane = static_cast<int>(rest % 64);
+  rest /= 64;
+  const int step = static_cast<int>(rest % nk);
+  rest /= nk;
+  const int slice = static_cast<int>(rest % nsl);
+  const int mat = static_cast<int>(rest / nsl);
+  const int r = lane & 15, g = lane >> 4;
+  const int k0 = step * kKS + 32 * j + 8 * g;
+  if (k0 >= K) return;  // padding past K
+  const int row = gate_up ? (r < 8 ? slice * 8 + r : N / 2 + slice * 8 + r - 8) : slice * 16 + r;
+  const uint8_t* blk = packed + static_cast<size_t>(mat) * pack_bytes(N, K) +
+                       (static_cast<size_t>(slice) * nk + step) * kPackBlock;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + lane * 16 + 4 * j);
+  const uint32_t sb = *reinterpret_cast<const uint32_t*>(blk + kPackScales + (2 * r + (j >> 1)) * 4);
+  const uint4 v = dequant8_pairs(w, bf16_to_f32(sb & 0xFFFFu), bf16_to_f32(sb >> 16));
+  *reinterpret_cast<uint4*>(out + (static_cast<size_t>(mat) * N + row) * K + k0) = v;
+}
+
+hipError_t launch_dequant_packed(int nmat, int N, int K, int gate_up, const uint8_t* packed,
+                                 uint16_t* out, hipStream_t stream) {
+  const long long total = static_cast<long long>(nmat) * (N / 16) * pack_steps(K) * 64 * 4;
+  hipLaunchKernelGGL(dequant_packed_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, stream, nmat, N, K, gate_up, packed, out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

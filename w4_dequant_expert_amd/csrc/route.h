@@ -52,6 +52,10 @@ hipError_t launch_combine(int T, int H, int k, int n_shared, const float* topk_w
                           uint32_t* status, hipStream_t stream);
 hipError_t launch_dequant(int rows, int K, const uint8_t* q, const uint16_t* s, const uint16_t* b,
                           uint16_t* out, hipStream_t stream);
+hipError_t launch_dequant_packed(int nmat, int N, int K, int gate_up, const uint8_t* packed,
+                                 uint16_t* out, hipStream_t stream);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                             hipStream_t stream);
 hipError_t launch_pack(int nmat, int N, int K, int gate_up, const uint8_t* q, const uint16_t* s,
                        const uint16_t* b, uint8_t* out, hipStream_t stream);
 

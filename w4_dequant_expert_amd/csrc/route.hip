@@ -571,22 +571,31 @@ __device__ void finish_tables(int T, int E, int k, int n_shared, int tile_m_max,
   __syncthreads();
   if (!write) return;  // only the offsets are needed
 
-  // block map: blocks per group, scanned into each group's first block
+  // block map: blocks per group, scanned into each group's first block.
+  // Thread g scans group g (g < 1024); with 1024 routed experts and a shared
+  // expert there are 1025 groups, and the last one (the shared group, index
+  // E = 1024) follows the scan: its first block is the scan's total.
   const int groups = E + (n_shared ? 1 : 0);
+  const int scanned = min(groups, 1024);
   int nb = 0;
-  if (tid < groups) {
+  if (tid < scanned) {
     const int c = s_cnt[tid];
     nb = (c + tile_m_max - 1) / tile_m_max;
   }
   int nb_total = 0;
   const int bstart = block_exclusive_scan(nb, tmp, &nb_total);
-  if (tid < groups) s_bstart[tid] = bstart;
+  if (tid < scanned) s_bstart[tid] = bstart;
   if (tid == 0) {
+    for (int g = scanned; g < groups; ++g) {  // at most one group
+      s_bstart[g] = nb_total;
+      nb_total += (s_cnt[g] + tile_m_max - 1) / tile_m_max;
+    }
     s_bstart[groups] = nb_total;
     if (nb_total > max_blocks) status_set(status, MOE_STATUS_BLOCK_OVERFLOW);
     *n_blocks = min(nb_total, max_blocks);
   }
   __syncthreads();
+  nb_total = s_bstart[groups];  // thread 0 may have added the last group
   const int nwrite = min(nb_total, max_blocks);
   for (int b = tid; b < nwrite; b += 1024) {
     int lo = 0, hi = groups - 1;  // last group whose first block is <= b

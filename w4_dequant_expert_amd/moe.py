@@ -21,7 +21,8 @@ STATUS_NAN_LOGIT, STATUS_BAD_INDEX, STATUS_BLOCK_OVERFLOW = 1, 2, 4
 
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_bytes", "moe_route",
             "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
-            "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_packed_bytes", "moe_w4_pack")
+            "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_dequant_packed", "moe_w4_packed_bytes",
+            "moe_w4_pack", "moe_read_probe")
 
 
 class Dims(ctypes.Structure):
@@ -87,6 +88,11 @@ def lib():
         L.moe_combine.argtypes = [P(Dims), P(RouteOut), vp, vp, vp]
         L.moe_w4_dequant.restype = ctypes.c_int
         L.moe_w4_dequant.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
+        L.moe_w4_dequant_packed.restype = ctypes.c_int
+        L.moe_w4_dequant_packed.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, vp, vp, vp]
+        L.moe_read_probe.restype = ctypes.c_int
+        L.moe_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int32, vp]
         L.moe_w4_packed_bytes.restype = ctypes.c_size_t
         L.moe_w4_packed_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
         L.moe_w4_pack.restype = ctypes.c_int
@@ -179,6 +185,16 @@ def moe_combine(d: Dims, out: RouteOut, y_slots, y, stream=None):
 def moe_w4_dequant(rows: int, K: int, q, s, b, out, stream=None):
     _check(lib().moe_w4_dequant(rows, K, _ptr(q), _ptr(s), _ptr(b), _ptr(out), _stream(stream)),
            "moe_w4_dequant")
+
+
+def moe_w4_dequant_packed(n: int, rows: int, K: int, gate_up: bool, packed, out, stream=None):
+    _check(lib().moe_w4_dequant_packed(n, rows, K, 1 if gate_up else 0, _ptr(packed), _ptr(out),
+                                       _stream(stream)), "moe_w4_dequant_packed")
+
+
+def moe_read_probe(src, nbytes: int, sink, workgroups: int, stream=None):
+    _check(lib().moe_read_probe(_ptr(src), nbytes, _ptr(sink), workgroups, _stream(stream)),
+           "moe_read_probe")
 
 
 def moe_w4_packed_bytes(rows: int, K: int) -> int:
