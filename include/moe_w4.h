@@ -183,6 +183,28 @@ int moe_route(const moe_dims *d, const uint16_t *x, const float *w_router, const
               const moe_route_out *out, void *stream);
 
 /*
+ * moe_route_no_alloc - moe_route for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same outputs, with the routing
+ * scratch taken from an array of MOE_NO_ALLOC_WS_BYTES the library owns on
+ * each device instead of out->ws (out->ws and out->ws_bytes are ignored and
+ * may be NULL / 0).  It calls no allocator.
+ *   - Returns MOE_EWS when the call needs more scratch than the array holds
+ *     (moe_route_ws_bytes without the exported-score region: 4 MiB covers up
+ *     to 2048 tokens at 256 experts with scores not exported).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *     device (two streams, two threads) race and must be serialised by the
+ *     caller.  The kernels clear what they accumulate into, so the contents
+ *     left by an earlier call do not matter.
+ *   - The array is held for the life of the process on every device the
+ *     library is used on.  The first call on a device looks up the array's
+ *     device address (a runtime query, not an allocation).
+ */
+#define MOE_NO_ALLOC_WS_BYTES (4u << 20)
+int moe_route_no_alloc(const moe_dims *d, const uint16_t *x, const float *w_router,
+                       const float *logit_bias, const moe_route_out *out, void *stream);
+
+/*
  * moe_w4_gate_up - grouped gate/up GEMM with the 4-bit weights reconstructed
  * tile by tile inside the kernel (never written out), float32 accumulation and
  * SwiGLU in the epilogue [LB, "Prefill: ..."].  For every block of the map:

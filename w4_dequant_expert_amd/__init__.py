@@ -24,6 +24,7 @@ from .moe import (  # noqa: F401
     moe_grouped_w4_ffn,
     moe_max_blocks,
     moe_route,
+    moe_route_no_alloc,
     moe_route_ws_bytes,
     moe_routed_w4_ffn,
     moe_shared_w4_ffn,

@@ -5,10 +5,21 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "route.h"
 
 using namespace moe;
+
+// ---------------------------------------------------------------------------
+// Library-owned routing scratch for moe_route_no_alloc.  The array lives in
+// the code object, so every GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses the array's name as an address (on
+// the host it only names the symbol): its device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and kept here.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MOE_NO_ALLOC_WS_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -179,6 +190,27 @@ int enqueue_route(const moe_dims& d, const uint16_t* x, const float* w_router,
   return launched(launch_route(d, x, w_router, logit_bias, rb, stream));
 }
 
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_ptr(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return MOE_EDEVICE;
+      p = static_cast<char*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,6 +249,19 @@ int moe_route(const moe_dims* d, const uint16_t* x, const float* w_router, const
   if ((rc = check_device())) return rc;
   return enqueue_route(*d, x, w_router, logit_bias, out, static_cast<char*>(out->ws), L,
                        static_cast<hipStream_t>(stream));
+}
+
+int moe_route_no_alloc(const moe_dims* d, const uint16_t* x, const float* w_router,
+                       const float* logit_bias, const moe_route_out* out, void* stream) {
+  int rc = validate_route_args(d, x, w_router, logit_bias, out, false);
+  if (rc) return rc;
+  const WsLayout L = ws_layout(*d, out->logits == nullptr);
+  if (L.total > kScratchBytes) return MOE_EWS;
+  if (d->T == 0) return MOE_OK;
+  if ((rc = check_device())) return rc;
+  char* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  return enqueue_route(*d, x, w_router, logit_bias, out, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int moe_w4_gate_up(const moe_dims* d, const uint16_t* x, const moe_route_out* r,

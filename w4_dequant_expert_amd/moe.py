@@ -17,9 +17,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_w4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWS, MOE_EDEVICE, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
+NO_ALLOC_WS_BYTES = 4 << 20   # MOE_NO_ALLOC_WS_BYTES
 STATUS_NAN_LOGIT, STATUS_BAD_INDEX, STATUS_BLOCK_OVERFLOW = 1, 2, 4
 
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_bytes", "moe_route",
+            "moe_route_no_alloc",
             "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
             "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_dequant_packed", "moe_w4_packed_bytes",
             "moe_w4_pack", "moe_read_probe")
@@ -74,6 +76,8 @@ def lib():
         L.moe_route_ws_bytes.argtypes = [P(Dims)]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [P(Dims), vp, vp, vp, P(RouteOut), vp]
+        L.moe_route_no_alloc.restype = ctypes.c_int
+        L.moe_route_no_alloc.argtypes = [P(Dims), vp, vp, vp, P(RouteOut), vp]
         L.moe_w4_gate_up.restype = ctypes.c_int
         L.moe_w4_gate_up.argtypes = [P(Dims), vp, P(RouteOut), P(Bank), P(Bank), vp, vp]
         L.moe_w4_down.restype = ctypes.c_int
@@ -146,6 +150,11 @@ def moe_route_ws_bytes(d: Dims) -> int:
 def moe_route(d: Dims, x, w_router, logit_bias, out: RouteOut, stream=None):
     _check(lib().moe_route(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(logit_bias),
                            ctypes.byref(out), _stream(stream)), "moe_route")
+
+
+def moe_route_no_alloc(d: Dims, x, w_router, logit_bias, out: RouteOut, stream=None):
+    _check(lib().moe_route_no_alloc(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                    ctypes.byref(out), _stream(stream)), "moe_route_no_alloc")
 
 
 def moe_w4_gate_up(d: Dims, x, out: RouteOut, routed: Bank, shared, h, stream=None):
