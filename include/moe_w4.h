@@ -63,7 +63,7 @@ extern "C" {
  *   E          routed experts, 1..1024
  *   k          experts selected per token, 1..min(E, 32)
  *   n_shared   always-on shared experts, 0 or 1 (same shape as a routed expert)
- *   tile_m_max largest GEMM tile height, a multiple of tile_gran in 16..128
+ *   tile_m_max largest GEMM tile height, a multiple of tile_gran in 16..256
  *   tile_gran  tile height granularity, 16 or 32
  * A slot is (token t, rank j < k) with id t*k + j.  The grouped GEMMs work on
  * Rows = T*k + n_shared*T rows: the routed slots in expert order, then one

@@ -56,7 +56,7 @@ def test_max_blocks_and_workspace():
 
 @pytest.mark.parametrize("field,value", [("H", 96), ("I", 0), ("E", 0), ("E", 2000), ("k", 0),
                                          ("k", 33), ("n_shared", 2), ("tile_m_max", 24),
-                                         ("tile_m_max", 256), ("tile_gran", 8), ("T", -1)])
+                                         ("tile_m_max", 272), ("tile_gran", 8), ("T", -1)])
 def test_invalid_dims_rejected(field, value):
     d = full(4)
     setattr(d, field, value)

@@ -372,7 +372,7 @@ def test_tiny_layer_full_parity():
     check_layer("tiny16", banks=(c["routed"], c["shared"], rd, sd))
 
 
-@pytest.mark.parametrize("tile_m_max", [16, 32, 64, 128])
+@pytest.mark.parametrize("tile_m_max", [16, 32, 64, 128, 256])
 def test_tiny_layer_tiles(tile_m_max):
     c = build_config("tiny16", T=150)
     rd, sd = moe.DeviceBank(c["routed"]), moe.DeviceBank(c["shared"])
@@ -398,11 +398,16 @@ def test_prefill512_all_tokens(full_banks, tile_m_max):
 
 
 @pytest.mark.timeout(300)
-def test_prefill2048_zipf_all_tokens(full_banks):
-    """The skewed 2048-token workload at the benchmark's tile bound, every token."""
-    _, g, _ = check_layer("prefill2048_zipf", banks=full_banks)
+@pytest.mark.parametrize("tile_m_max", [128, 256])
+def test_prefill2048_zipf_all_tokens(full_banks, tile_m_max):
+    """The skewed 2048-token workload, every token; 256 is the tile bound the
+    benchmark runs it with (blocks of up to 256 rows in the 256-row kernel)."""
+    _, g, _ = check_layer("prefill2048_zipf", tile_m_max=tile_m_max, banks=full_banks,
+                          label=f"zipf M={tile_m_max}")
     counts = g["counts"]
     assert (counts == 0).sum() >= 1 and (counts > 200).sum() >= 1
+    if tile_m_max == 256:
+        assert (g["blocks"][:, 3] > 128).sum() >= 10   # the 256-row kernel has work
 
 
 @pytest.mark.timeout(300)
@@ -536,7 +541,8 @@ def test_grouped_ffn_matches_separate_calls(full_banks, T):
 
 @pytest.mark.parametrize("cfg,T,tile_m_max", [("decode1", 1, 32), ("decode1", 5, 32),
                                                ("decode1", 48, 32), ("prefill512", 512, 32),
-                                               ("decode1", 300, 128), ("prefill2048_zipf", 2048, 128)])
+                                               ("decode1", 300, 128), ("prefill2048_zipf", 2048, 128),
+                                               ("prefill2048_zipf", 2048, 256)])
 def test_split_ffn_matches_grouped(full_banks, cfg, T, tile_m_max):
     """The shared expert on a second stream, concurrent with routing, then the
     routed experts (moe_shared_w4_ffn + moe_routed_w4_ffn): h and y_slots equal
@@ -616,6 +622,9 @@ def test_routing_batch_sizes(full_banks, T):
     (2112, 64, 16, 2, 1, 3, 32),    # short batch: a wave with more steps than one load chunk
     (192, 64, 5, 5, 1, 200, 128),   # tall tiles (every expert 200 rows: blocks of 100) with K tails
     (1088, 320, 24, 4, 1, 300, 128),  # tall and small tiles, K tails in both GEMMs
+    (192, 64, 5, 5, 1, 250, 256),   # 256-row tiles (one block of 250 rows per group), K tails
+    (1088, 320, 24, 4, 1, 1000, 256),  # 160..256-row and shorter tiles, K tails in both GEMMs
+    (256, 128, 8, 2, 1, 700, 256),  # 175-row groups: five row tiles
     (256, 128, 300, 8, 1, 5, 32),   # more than 256 experts, short batch: one-kernel scores, wide top-k
     (256, 128, 300, 8, 1, 64, 32),  # more than 256 experts: tiled scores, wide top-k, scan
     (128, 64, 1024, 4, 1, 5, 16),   # 1024 experts and a shared one: 1025 groups in the block map

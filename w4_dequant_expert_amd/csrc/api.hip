@@ -51,7 +51,7 @@ int validate_dims(const moe_dims* d) {
   if (d->k < 1 || d->k > kMaxK || d->k > d->E) return MOE_EINVAL;
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_EINVAL;
   if (d->tile_gran != 16 && d->tile_gran != 32) return MOE_EINVAL;
-  if (d->tile_m_max < 16 || d->tile_m_max > 128 || d->tile_m_max % d->tile_gran) return MOE_EINVAL;
+  if (d->tile_m_max < 16 || d->tile_m_max > 256 || d->tile_m_max % d->tile_gran) return MOE_EINVAL;
   return MOE_OK;
 }
 

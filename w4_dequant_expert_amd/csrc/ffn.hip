@@ -655,6 +655,7 @@ __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* _
   BlockInfo bi;
   if (!block_info<GATE_UP>(a, bi, 2 * kT4CT * kT4Waves)) return;
   if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
+  if (bi.tm > kTallM) return;  // a block of more than 128 rows: the 256-row kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
   switch ((bi.tm + 31) >> 5) {
     case 1: tall4_block<1, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
@@ -692,6 +693,216 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
   __shared__ int s_tok[kTallM];
   tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
+}
+
+// ---------------------------------------------------------------------------
+// Tall-tile kernel for blocks of 160..256 rows: MT = 5..8 row tiles of 32 on
+// v_mfma_f32_32x32x16_bf16 with ONE 32-column tile per wave, so that each
+// rebuilt weight feeds MT (up to eight) MFMAs -- half the rebuild work per
+// MFMA of the four-row-tile kernel, whose rebuild is what keeps the matrix
+// core waiting there.  A workgroup of four waves covers 8 slices.
+//   - The activation tile of up to 256 rows is staged in LDS one half-step (64
+//     inputs, 128 bytes a row) at a time, in two buffers of 32 KB, so two
+//     workgroups still share a CU.  Half-step hs+1 is copied (global_load_lds)
+//     into the buffer half-step hs-1 read while half-step hs computes.
+//   - A row's eight 16-byte chunks are stored XOR-swizzled by (row / 2) mod 8:
+//     with 128-byte rows, sixteen consecutive rows then cover every LDS bank
+//     once, so the 32-row MFMA reads are conflict-free.
+//   - The weight codes of a step are loaded into registers one step ahead
+//     (at its first half-step) and rebuilt one k-chunk ahead of the MFMAs.
+// Half-steps entirely past K (K mod 128 = 64) are skipped.
+// ---------------------------------------------------------------------------
+constexpr int kTall8M = 256;
+constexpr int kHalfK = 64;                            // inputs per staged half-step
+constexpr int kTall8Buf = kTall8M * kHalfK * 2;       // bytes of one staged half-step
+static_assert(kTall8Buf == kTallBuf, "both tall kernels stage 32 KB buffers");
+
+template <int MT, bool GATE_UP>
+__device__ __forceinline__ void tall8_block(const GemmArgs& a, const BlockInfo& bi,
+                                            const uint16_t* __restrict__ src,
+                                            uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
+                                            int* s_tok) {
+  constexpr int NCP = MT;  // activation copies per wave per half-step (8 rows each)
+  const int K = GATE_UP ? a.H : a.I;
+  const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
+  const int nk = pack_steps(K);
+  const int nh = 2 * nk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int row0 = bi.row0, rows = bi.rows;
+
+  // one 32-column tile (two slices) per wave; nslices is even, so both
+  // slices of a tile are in or both out
+  const int c_first = bi.nt * (2 * kT4Waves) + wave * 2;
+  const size_t sstride = static_cast<size_t>(nk) * kPackBlock;
+  // lane l reads column n = l mod 32 of the tile: row n mod 16 of slice n/16;
+  // k-chunk j of a step holds inputs 16j + 8h .. +7 (h = l/32)
+  const int h = lane >> 5, nrow = lane & 15, nsl = (lane >> 4) & 1;
+  const uint8_t* cbase = bi.P + static_cast<size_t>(min(c_first, nslices - 2) + nsl) * sstride;
+  auto load_codes = [&](int s, RawCodes& rc) {
+    const uint8_t* blk = cbase + static_cast<size_t>(min(s, nk - 1)) * kPackBlock;
+    rc.ce = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16);
+    rc.co = *reinterpret_cast<const uint4*>(blk + (16 * h + nrow) * 16 + 512);
+    rc.g = *reinterpret_cast<const uint2*>(blk + kPackScales + nrow * 8);
+  };
+  auto to_tile = [&](const RawCodes& rc, TileCodes& tc) {
+    tc.q[0] = rc.ce.x; tc.q[1] = rc.co.x;
+    tc.q[2] = rc.ce.y; tc.q[3] = rc.co.y;
+    tc.q[4] = rc.ce.z; tc.q[5] = rc.co.z;
+    tc.q[6] = rc.ce.w; tc.q[7] = rc.co.w;
+    tc.sb[0] = rc.g.x;
+    tc.sb[1] = rc.g.y;
+  };
+  auto rebuild_j = [&](const TileCodes& tc, int j) -> bf16x8 {
+    const uint32_t sbw = tc.sb[j >> 2];
+    return as_bf16x8(dequant8_pairs(tc.q[j], bf16_to_f32(sbw & 0xFFFFu), bf16_to_f32(sbw >> 16)));
+  };
+
+  // Activation copies: copy i of wave w moves tile rows 8q .. 8q+7, q = 4i + w,
+  // into LDS bytes [1024 q, 1024 q + 1024); lane -> row 8q + lane/8, stored at
+  // chunk position lane % 8, which holds the row's chunk (lane % 8) ^ ((row /
+  // 2) mod 8).  (row / 2) mod 8 is the same for every copy of a lane.
+  const int rsub = lane >> 3;
+  const int cg = (lane & 7) ^ (((8 * wave + rsub) >> 1) & 7);
+  const uint16_t* arow[NCP];  // each copy's source row, set once the block's tokens are known
+  auto issue_a = [&](int hs, uint8_t* buf) {
+    const int kk = min(min(hs, nh - 1) * kHalfK + cg * 8, K - 8);
+#pragma unroll
+    for (int i = 0; i < NCP; ++i)
+      __builtin_amdgcn_global_load_lds(arow[i] + kk, buf + (kT4Waves * i + wave) * 1024, 16, 0, 0);
+  };
+  // MFMA A reads: row l mod 32 of a row tile, chunk 2j + h of the half-step
+  const int arow_l = lane & 31;
+  int aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = arow_l * (kHalfK * 2) + (((2 * j + h) ^ ((arow_l >> 1) & 7)) * 16);
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mt][i] = 0.0f;
+
+  bf16x8 bq[2];
+  TileCodes tc;
+  RawCodes rnext;
+  // Issue order: the first half-step of step s issues the copies of half-step
+  // 2s+1, then the codes of step s+1 (three loads); the second issues the
+  // copies of 2s+2.  So the second half-step can wait for its activations
+  // with the codes still in flight, and the codes are waited for only before
+  // the step's last k-chunk rebuilds the next step's first weights.
+  constexpr int kCodeLoads = 3;
+  auto half = [&](int hs, uint8_t* acur, uint8_t* anew) {
+    const bool first = (hs & 1) == 0;
+    if (first) wait_vmcnt<0>();           // activations of half-step hs
+    else wait_vmcnt<kCodeLoads>();        // activations of half-step hs; codes may fly on
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(hs + 1, anew);
+    if (first) load_codes((hs >> 1) + 1, rnext);
+    __builtin_amdgcn_sched_barrier(0);
+    if (hs * kHalfK >= K) {  // past K: nothing to multiply (uniform)
+      if (!first) {
+        wait_vmcnt<NCP>();  // codes of the next step
+        to_tile(rnext, tc);
+        bq[0] = rebuild_j(tc, 0);
+      }
+      return;
+    }
+    bf16x8 af[2][MT];
+    auto read_a = [&](int j, bf16x8 (&f)[MT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        f[mt] = *reinterpret_cast<const bf16x8*>(acur + mt * 32 * (kHalfK * 2) + aoff[j]);
+    };
+    read_a(0, af[0]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = (first ? 0 : 4) + jj;  // k-chunk within the step
+      if (jj < 3) read_a(jj + 1, af[(jj + 1) & 1]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[jj & 1][mt], bq[j & 1], acc[mt], 0, 0, 0);
+      if (j < 7) {
+        bq[(j + 1) & 1] = rebuild_j(tc, j + 1);
+        // the operand of the MFMAs above stays live past the rebuild (other
+        // registers, no wait for those MFMAs to read theirs)
+        asm volatile("" ::"v"(bq[j & 1]));
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<NCP>();  // codes of the next step
+        __builtin_amdgcn_sched_barrier(0);
+        to_tile(rnext, tc);
+        bq[0] = rebuild_j(tc, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The codes of step 0 do not depend on the block's tokens: they are in
+  // flight while the token list is gathered.
+  RawCodes r0;
+  load_codes(0, r0);
+  if (GATE_UP) {
+    block_tokens(a, bi, s_tok);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int r = min(8 * (kT4Waves * i + wave) + rsub, rows - 1);
+    const int srow = GATE_UP ? max(s_tok[r], 0) : row0 + r;
+    arow[i] = src + static_cast<size_t>(srow) * K;
+  }
+  issue_a(0, As0);
+  wait_vmcnt<0>();
+  to_tile(r0, tc);
+  bq[0] = rebuild_j(tc, 0);
+  int hs = 0;
+  for (; hs + 1 < nh; hs += 2) {
+    half(hs, As0, As1);
+    half(hs + 1, As1, As0);
+  }
+  wait_vmcnt<0>();  // the last half-step's spare copies land before the LDS is released
+
+  if (c_first >= nslices) return;
+  const int c = c_first + nsl;
+  const int n16 = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+      const size_t r = static_cast<size_t>(row0 + m);
+      const float v = acc[mt][i];
+      if (GATE_UP) {
+        const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
+        if (n16 < 8 && m < rows) {
+          const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+          out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
+        }
+      } else if (m < rows) {
+        out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2))) void w4_gemm_tall8_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kTall8Buf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kTall8Buf];
+  __shared__ int s_tok[kTall8M];
+  BlockInfo bi;
+  if (!block_info<GATE_UP>(a, bi, 2 * kT4Waves)) return;
+  if (bi.tm <= kTallM) return;  // the four-row-tile kernel owns it
+  if (!block_valid<GATE_UP>(a, bi, kTall8M)) return;
+  switch ((bi.tm + 31) >> 5) {
+    case 5: tall8_block<5, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 6: tall8_block<6, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    case 7: tall8_block<7, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+    default: tall8_block<8, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -890,7 +1101,9 @@ static hipError_t launch_gemv(const GemmArgs& a, const uint16_t* src, uint16_t* 
 }
 
 // Tall-tile kernel variant for a tile height bound (0: no tile exceeds kSmallM).
-int gemm_m_max_for(int tile_m_max) { return tile_m_max <= kSmallM ? 0 : 128; }
+int gemm_m_max_for(int tile_m_max) {
+  return tile_m_max <= kSmallM ? 0 : tile_m_max <= kTallM ? kTallM : kTall8M;
+}
 
 template <bool GATE_UP>
 static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src, uint16_t* out,
@@ -912,6 +1125,10 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
       hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 2>),
                          dim3(static_cast<unsigned>(b8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves))),
                          dim3(64 * kSmallWaves), 0, stream, ga, src, out);
+    } else if (tm > kTallM) {
+      hipLaunchKernelGGL((w4_gemm_tall8_kernel<GATE_UP>),
+                         dim3(static_cast<unsigned>(b8 * n_tiles<GATE_UP>(a, 2 * kT4Waves))),
+                         dim3(kT4Threads), 0, stream, ga, src, out);
     } else {
       hipLaunchKernelGGL((w4_gemm_tall4_shared_kernel<GATE_UP>),
                          dim3(static_cast<unsigned>(b8 * n_tiles<GATE_UP>(a, 2 * kT4CT * kT4Waves))),
@@ -931,6 +1148,10 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
     else
       hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 0>), grid_small,
                          dim3(64 * kSmallWaves), 0, stream, ga, src, out);
+  }
+  if (m_max > kTallM) {  // blocks of 160..256 rows first: they hold most of the work
+    const dim3 grid8(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4Waves)));
+    hipLaunchKernelGGL((w4_gemm_tall8_kernel<GATE_UP>), grid8, dim3(kT4Threads), 0, stream, ga, src, out);
   }
   if (m_max) {
     const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, 2 * kT4CT * kT4Waves)));
