@@ -262,6 +262,9 @@ def decode_leg(copies=40):
     # as in the captured graph
     w_eager, _ = time_workload(wl, 200, 20, fresh, overlap=False)
     step_ms = graph_ms(lambda i: wl.step(i, x=fresh[i], overlap=False), copies)
+    # the shared expert's FFN on a second stream (a parallel branch of the
+    # graph), concurrent with routing; then the routed experts and the combine
+    overlap_ms = graph_ms(lambda i: wl.step(i, x=fresh[i], overlap=True), copies)
     L = wl.layer
     d = L.dims(1)
     x0 = fresh[0]
@@ -283,6 +286,7 @@ def decode_leg(copies=40):
     gemm_gbs = (wk["bytes_gate_up"] + wk["bytes_down"]) / g_s / 1e9
     out = dict(
         tokens_per_s=1.0 / (step_ms * 1e-3), ms_per_step=step_ms, timing="hip graph replay",
+        shared_overlap_ms_per_step=round(overlap_ms, 5),
         eager_tokens_per_s=200 / w_eager,
         route_ms=round(route_ms, 5), ffn_ms=round(ffn_ms, 5), combine_ms=round(cb_ms, 5),
         gate_up_ms=round(gu_ms, 5), down_ms=round(dn_ms, 5),
@@ -323,31 +327,121 @@ def small_batch_leg(Ts=(2, 4, 8), copies=40):
     return out
 
 
-def ablation_leg(copies, steps=50):
-    """Two of the pages' ablations at 512 tokens.
-    - Unfused reconstruction: expanding every touched expert's 4-bit weights to
-      bfloat16 in memory (moe_w4_dequant over the canonical layout), which an
-      unfused path must do before its GEMMs; compared with the fused layer.
-    - Host-synchronised routing: the same layer call with the block count read
-      back to the host (a device-to-host copy and a wait) between routing and
-      the GEMMs, as a host-driven expert loop needs."""
+def host_route_tables(topk_idx, E, k, n_shared, tile_m_max, tile_gran):
+    """The routing steps after top-k (histogram, exclusive scan, stable scatter,
+    block map) computed on the host with numpy, as an engine that brings the
+    selections back to the CPU does: the host-synced side of the routing
+    ablation.  Same rules as the device tables (checked against them)."""
+    import numpy as np
+    T = topk_idx.shape[0]
+    flat = topk_idx.reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    np.cumsum(counts, out=offsets[1:])
+    sorted_slot = np.argsort(flat, kind="stable").astype(np.int32)
+    slot_pos = np.empty_like(sorted_slot)
+    slot_pos[sorted_slot] = np.arange(T * k, dtype=np.int32)
+    blocks = []
+    for g, c, first in [(e, int(counts[e]), int(offsets[e])) for e in range(E)] + \
+            ([(E, T, T * k)] if n_shared else []):
+        if c == 0:
+            continue
+        nb = -(-c // tile_m_max)
+        base, rem = divmod(c, nb)
+        tm = -(-(base + (rem > 0)) // tile_gran) * tile_gran
+        for i in range(nb):
+            rows = base + (i < rem)
+            blocks.append((g, first, rows, tm))
+            first += rows
+    return counts, offsets, sorted_slot, slot_pos, np.array(blocks, dtype=np.int32).reshape(-1, 4)
+
+
+def ablation_leg(copies, steps=30):
+    """The pages' two MoE ablations at 512 tokens, end to end, each against the
+    library's own layer call (moe_route, moe_grouped_w4_ffn, moe_combine:
+    routing on the GPU, reconstruction fused into the grouped GEMMs).
+    - Host-synced routing: the selections (top-k) are copied to the host, the
+      histogram, scan, scatter and block map are built there (numpy), copied
+      back, and the same GEMM and combine kernels run on them.  (moe_route
+      still builds its own tables on the GPU; the host ones replace them.)
+    - Unfused reconstruction: every call expands the packed 4-bit weights of
+      the 257 experts to bfloat16 in memory (moe_w4_dequant_packed, the same
+      reconstruction as the tall GEMM), then runs batched bfloat16 GEMMs on
+      them (torch.bmm over each expert's rows, padded to 32; the shared expert
+      as plain GEMMs), SwiGLU and the weighted combine as tensor operations."""
     import numpy as np
     import torch
 
     import w4_dequant_expert_amd as moe
     wl = Workload("prefill512", copies)
-    sh, c = wl.sh, wl.c
+    sh = wl.sh
     L = wl.layer
-    nb_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    T, E, k, H, I = wl.T, sh.E, sh.k, sh.H, sh.I
+    rt = L.rt
+    idx_host = torch.empty((T, k), dtype=torch.int32, pin_memory=True)
+    tables_ok = []
 
-    def synced(i):
+    def host_synced(i):
         r, s_, wr = wl.copies[i % len(wl.copies)]
         L.w_router = wr
         d = L.route(wl.x)
-        nb_host.copy_(L.rt.n_blocks[:1], non_blocking=True)
+        idx_host.copy_(rt.topk_idx, non_blocking=True)
         torch.cuda.current_stream().synchronize()
+        counts, offsets, ss, sp, blocks = host_route_tables(idx_host.numpy(), E, k, sh.n_shared,
+                                                            wl.tile_m_max, 16)
+        if not tables_ok:  # the host tables are the device's, once checked
+            tables_ok.append(np.array_equal(ss, rt.sorted_slot.cpu().numpy()) and
+                             np.array_equal(blocks, rt.blocks[:len(blocks)].cpu().numpy()))
+        rt.counts.copy_(torch.from_numpy(counts), non_blocking=True)
+        rt.offsets.copy_(torch.from_numpy(offsets), non_blocking=True)
+        rt.sorted_slot.copy_(torch.from_numpy(ss), non_blocking=True)
+        rt.slot_pos.copy_(torch.from_numpy(sp), non_blocking=True)
+        rt.blocks[:len(blocks)].copy_(torch.from_numpy(blocks), non_blocking=True)
+        rt.n_blocks.fill_(len(blocks))
         L.ffn(d, wl.x, r, s_)
         L.combine(d, wl.y)
+
+    # unfused: expanded bf16 weights, batched GEMMs over the rows in expert
+    # order, each expert's rows padded to P (every expert has at most P rows at
+    # 512 tokens); the shared expert as plain GEMMs over all tokens.  Every
+    # batched product takes contiguous operands only.
+    base_r, base_s = wl.copies[0][0], wl.copies[0][1]
+    P = 32
+    w_gu = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device="cuda")
+    w_dn = torch.empty((E, H, I), dtype=torch.bfloat16, device="cuda")
+    s_gu = torch.empty((1, 2 * I, H), dtype=torch.bfloat16, device="cuda")
+    s_dn = torch.empty((1, H, I), dtype=torch.bfloat16, device="cuda")
+    xb = wl.x.view(torch.bfloat16)
+    F = torch.nn.functional
+
+    def expand():
+        moe.moe_w4_dequant_packed(E, 2 * I, H, True, base_r.t["gu"], w_gu)
+        moe.moe_w4_dequant_packed(E, H, I, False, base_r.t["dn"], w_dn)
+        moe.moe_w4_dequant_packed(1, 2 * I, H, True, base_s.t["gu"], s_gu)
+        moe.moe_w4_dequant_packed(1, H, I, False, base_s.t["dn"], s_dn)
+
+    def unfused_gemms():
+        expert = torch.repeat_interleave(torch.arange(E, device="cuda"), rt.counts.long(),
+                                         output_size=T * k)
+        pos = torch.arange(T * k, device="cuda") - rt.offsets[:E].long()[expert]
+        pad = expert * P + pos                                          # padded row of each slot row
+        a = torch.zeros((E * P, H), dtype=torch.bfloat16, device="cuda")
+        a[pad] = xb.index_select(0, rt.sorted_slot.long() // k)
+        at = a.view(E, P, H).transpose(1, 2).contiguous()               # [E][H][P]
+        gt = torch.bmm(w_gu, at)                                        # [E][2I][P]
+        ht = (F.silu(gt[:, :I].float()) * gt[:, I:].float()).to(torch.bfloat16).contiguous()
+        yt = torch.bmm(w_dn, ht)                                        # [E][H][P]
+        ys = yt.transpose(1, 2).reshape(E * P, H)[pad]                  # rows in expert order
+        g2 = F.linear(xb, s_gu[0])                                      # shared expert
+        y_sh = F.linear((F.silu(g2[:, :I].float()) * g2[:, I:].float()).to(torch.bfloat16), s_dn[0])
+        sel = ys.index_select(0, rt.slot_pos.long()).view(T, k, H).float()
+        y = (sel * rt.topk_w.unsqueeze(-1)).sum(1) + y_sh.float()
+        return y.to(torch.bfloat16)
+
+    def unfused(i):
+        L.route(wl.x)
+        expand()
+        return unfused_gemms()
 
     def timed(fn):
         torch.cuda.synchronize()
@@ -356,47 +450,39 @@ def ablation_leg(copies, steps=50):
             fn(i)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps * 1e3
-    # warm the clocks on both paths, then alternate them (fused: GPU-resident
-    # routing, the headline path; synced: the block count read back first)
+    # warm the clocks, then alternate the paths
     for i in range(100):
         wl.step(i)
-    for i in range(20):
-        synced(i)
-    fused, syn = [], []
+    for i in range(10):
+        host_synced(i)
+    out = {}
+    L.w_router = wl.copies[0][2]
+    wl.step(0)  # the fused call on weight copy 0, then the unfused path on the same inputs
+    torch.cuda.synchronize()
+    assert int(rt.counts.max().item()) <= P
+    yf = wl.y.view(torch.bfloat16).float()
+    y_unf = unfused(0).float()
+    out["unfused_vs_fused_max_rel"] = float(((y_unf - yf).abs().max(1).values /
+                                             yf.abs().max(1).values).max())
+    fused, syn, unf, exp_only = [], [], [], []
     for _ in range(3):
         fused.append(timed(wl.step))
-        syn.append(timed(synced))
+        syn.append(timed(host_synced))
+        unf.append(timed(unfused))
+        exp_only.append(timed(lambda i: expand()))
     fused_ms, synced_ms = min(fused), min(syn)
-    # expansion of the touched experts' weights (every expert is touched at 512 tokens)
-    bank = c["routed"]
-    E, H, I = sh.E, sh.H, sh.I
-    canon = {k: torch.from_numpy(np.ascontiguousarray(bank[k]).view(np.uint8 if k.endswith("_q") else np.int16))
-             .to("cuda") for k in ("gu_q", "gu_s", "gu_b", "dn_q", "dn_s", "dn_b")}
-    gu_out = torch.empty((E * 2 * I, H), dtype=torch.int16, device="cuda")
-    dn_out = torch.empty((E * H, I), dtype=torch.int16, device="cuda")
-
-    def expand():
-        moe.moe_w4_dequant(E * 2 * I, H, canon["gu_q"], canon["gu_s"], canon["gu_b"], gu_out)
-        moe.moe_w4_dequant(E * H, I, canon["dn_q"], canon["dn_s"], canon["dn_b"], dn_out)
-    expand()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        expand()
-    e1.record()
-    torch.cuda.synchronize()
-    expand_ms = e0.elapsed_time(e1) / 10
-    expanded = (gu_out.numel() + dn_out.numel()) * 2
-    out = dict(
+    out.update(
         fused_layer_ms=round(fused_ms, 5),
         host_synced_routing_layer_ms=round(synced_ms, 5),
         gpu_resident_routing_speedup=synced_ms / fused_ms,
-        unfused_expand_ms=round(expand_ms, 5), unfused_expanded_bytes=expanded,
-        fused_over_unfused_expand_alone=expand_ms / fused_ms,
-        note="unfused_expand_ms is only the bf16 expansion of the 256 routed experts' weights "
-             "(the GEMMs an unfused path then runs come on top of it)")
-    del wl, canon, gu_out, dn_out
+        host_tables_match_device=bool(tables_ok and tables_ok[0]),
+        note="layer calls at 512 tokens, wall clock per call over 30 calls, best of 3 alternated "
+             "passes")
+    unf_ms, exp_ms = min(unf), min(exp_only)
+    out.update(unfused_layer_ms=round(unf_ms, 5), unfused_expand_ms=round(exp_ms, 5),
+               unfused_expanded_bytes=(w_gu.numel() + w_dn.numel() + s_gu.numel() + s_dn.numel()) * 2,
+               fused_dequant_speedup=unf_ms / fused_ms)
+    del wl, w_gu, w_dn, s_gu, s_dn
     torch.cuda.empty_cache()
     return out
 
