@@ -23,3 +23,4 @@ from .api import (  # noqa: F401
     relative_error,
     relative_error_elementwise,
 )
+from .gdn import gated_delta_scan  # noqa: F401

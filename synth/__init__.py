@@ -24,3 +24,4 @@ from .gen import (  # noqa: F401
     make_tokens,
 )
 from .configs import CONFIGS, LayerShape, FULL_SHAPE, TINY_SHAPE, build_config  # noqa: F401
+from .gdn import GDN_CONFIGS, GdnShape, build_gdn_config, make_gdn_inputs  # noqa: F401
