@@ -29,6 +29,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector, published (packed fp32 instructions)
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flops (one fused multiply-add) x 2.4 GHz:
+# the fp32 vector rate without packed instructions, which this build never emits
+PEAK_FP32_UNPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_prefill512.txt")
 DOMINANT = "w4_gemm_small_kernel<4, 2, true, 0>"   # the gate/up GEMM of the 512-token workload
 # Tile height bound per workload: uniform routing at 512 tokens gives every
@@ -53,7 +57,7 @@ def parse():
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this size (counter calibration)")
     p.add_argument("--only", choices=["prefill512", "prefill2048_zipf", "decode1", "chunked16384",
-                                      "small_batches", "ablations", "tile_sweep"],
+                                      "small_batches", "ablations", "tile_sweep", "gdn_prefill2048"],
                    default=None,
                    help="time a single workload (profiling runs)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
@@ -325,6 +329,54 @@ def decode_leg(copies=40):
         bytes_per_token=wk["bytes_layer"], weight_copies=copies)
     del wl
     return out
+
+
+def gdn_leg(reps=20, warmup=5):
+    """The Gated DeltaNet scan over the 2048-token sequence (16 key heads, 32
+    value heads of width 128): back-to-back launches timed with HIP events on
+    the stream they run on.  Algorithmic work per token, value head and state
+    element: the two dot products (2 fused multiply-adds) and the update (a
+    multiply and a fused multiply-add), 7 flops."""
+    import numpy as np
+    import torch
+
+    import w4_dequant_expert_amd as moe
+    from synth import build_gdn_config
+
+    c = build_gdn_config("gdn_prefill2048")
+    sh = c["shape"]
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+
+    q, k, v, g, b = (dev(c[n]) for n in ("q", "k", "v", "g", "beta"))
+    o = torch.empty((sh.T, sh.n_v_heads, sh.dv), dtype=torch.int16, device="cuda")
+    s_out = torch.empty((sh.n_v_heads, sh.dv, sh.dk), dtype=torch.float32, device="cuda")
+    d = moe.GdnDims(sh.T, sh.n_k_heads, sh.n_v_heads, sh.dk, sh.dv)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        moe.gdn_scan(d, q, k, v, g, b, None, s_out, o, stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 7.0 * sh.T * sh.n_v_heads * sh.dv * sh.dk
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(tokens_per_s=sh.T / (ms * 1e-3), ms_per_scan=ms, tokens=sh.T,
+                key_heads=sh.n_k_heads, value_heads=sh.n_v_heads, head_dim=sh.dk,
+                algorithmic_flops=flops, tflops=tflops,
+                frac_fp32_vector=tflops / PEAK_FP32_TFLOPS,
+                frac_fp32_vector_unpacked=tflops / PEAK_FP32_UNPACKED_TFLOPS,
+                state_bytes_kept_on_chip=sh.n_v_heads * sh.dv * sh.dk * 4)
 
 
 def small_batch_leg(Ts=(2, 4, 8), copies=40):
@@ -695,6 +747,9 @@ def main():
     if main_name == "ablations":
         print(json.dumps({"ablations_prefill512": ablation_leg(args.copies)}))
         return
+    if main_name == "gdn_prefill2048":
+        print(json.dumps({"gdn_prefill2048": gdn_leg()}))
+        return
     if main_name == "tile_sweep":  # tokens/s per tile-height bound (not in the default run)
         print(json.dumps({"tile_sweep": tile_sweep_leg(args.copies)}))
         return
@@ -720,6 +775,15 @@ def main():
             "avg_launch_ms": {"gate_up": dec["gate_up_ms"], "down": dec["down_ms"]},
             "stream_ceiling_gbs": dec["stream_ceiling"]["gbs"],
             "frac_of_stream_ceiling": dec["gemm_frac_of_stream_ceiling"]}
+        torch.cuda.empty_cache()
+        gd = gdn_leg()
+        extra["gdn_prefill2048"] = gd
+        sib["roofline_gdn_prefill2048"] = {
+            "bound": "alu", "kernel": "gdn_scan_kernel", "achieved": gd["tflops"],
+            "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": gd["frac_fp32_vector"],
+            "peak_without_packed_fp32": PEAK_FP32_UNPACKED_TFLOPS,
+            "frac_without_packed_fp32": gd["frac_fp32_vector_unpacked"],
+            "algorithmic_flops": gd["algorithmic_flops"], "avg_launch_ms": gd["ms_per_scan"]}
         torch.cuda.empty_cache()
         # the 2048-token GEMM-heavy leg last, directly before the headline
         wl2 = Workload("prefill2048_zipf", args.copies, None)

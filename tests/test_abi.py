@@ -12,19 +12,23 @@ import pytest
 import w4_dequant_expert_amd as moe
 from w4_dequant_expert_amd.moe import Bank, Dims, RouteOut
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "moe_w4.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+    """Every function declared in include/*.h (comments stripped)."""
+    names = set()
+    for fn in sorted(os.listdir(INCLUDE)):
+        if fn.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, fn)).read(), flags=re.S)
+            names.update(re.findall(r"\b((?:moe|gdn)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert "moe_route" in names and "moe_combine" in names and "moe_grouped_w4_ffn" in names
+    assert "gdn_scan" in names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -172,3 +176,31 @@ def test_block_bound_covers_1024_experts_with_shared():
     for T in (1, 5, 64, 300):
         d = moe.make_dims(T, 128, 64, 1024, 4, 1, 16, 16)
         assert moe.moe_max_blocks(d) == oracle.max_blocks(T, 1024, 4, 1, 16)
+
+
+def test_gdn_scan_validation_codes():
+    """gdn_scan rejects bad shapes, null and misaligned pointers before any
+    launch; T = 0 with no output state enqueues nothing."""
+    from w4_dequant_expert_amd.moe import GdnDims
+    L = moe.lib()
+    q, k, v, g, b, si, so, o = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, 0x70000, 0x80000
+
+    def call(d, **kw):
+        a = dict(q=q, k=k, v=v, g=g, b=b, si=si, so=so, o=o)
+        a.update(kw)
+        return L.gdn_scan(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"], a["b"], a["si"], a["so"],
+                          a["o"], None)
+
+    good = GdnDims(16, 2, 4, 128, 128)
+    for bad in (GdnDims(16, 2, 4, 64, 128), GdnDims(16, 2, 4, 128, 64), GdnDims(-1, 2, 4, 128, 128),
+                GdnDims((1 << 24) + 1, 2, 4, 128, 128), GdnDims(16, 0, 4, 128, 128),
+                GdnDims(16, 3, 4, 128, 128), GdnDims(16, 4, 2, 128, 128), GdnDims(16, 1, 1025, 128, 128)):
+        assert call(bad) == -1
+    assert L.gdn_scan(None, q, k, v, g, b, si, so, o, None) == -1
+    for name in ("q", "k", "v", "g", "b", "o"):
+        assert call(good, **{name: None}) == -1, name
+    for name in ("q", "k", "v", "o", "si", "so"):
+        assert call(good, **{name: 0x10008}) == -2, name
+    assert call(good, g=0x40002) == -2
+    assert call(GdnDims(0, 2, 4, 128, 128), q=None, k=None, v=None, g=None, b=None, o=None,
+                so=None) == 0

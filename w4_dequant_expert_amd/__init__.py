@@ -1,7 +1,7 @@
 """MI355X (gfx950) sparse MoE expert layer with fused groupwise-affine 4-bit weights.
 
-The compute lives in libmoe_w4.so (hand-written HIP, C ABI in include/moe_w4.h);
-this package only marshals arguments to it.
+The compute lives in libmoe_w4.so (hand-written HIP, C ABI in include/moe_w4.h
+and include/gdn_scan.h); this package only marshals arguments to it.
 """
 
 from .moe import (  # noqa: F401
@@ -9,6 +9,7 @@ from .moe import (  # noqa: F401
     DeviceBank,
     Dims,
     EXPORTED,
+    GdnDims,
     LIB_PATH,
     MoeError,
     MoeLayer,
@@ -17,6 +18,7 @@ from .moe import (  # noqa: F401
     STATUS_BAD_INDEX,
     STATUS_BLOCK_OVERFLOW,
     STATUS_NAN_LOGIT,
+    gdn_scan,
     lib,
     make_dims,
     moe_abi_version,

@@ -22,10 +22,12 @@ constexpr size_t kScratchBytes = MOE_NO_ALLOC_WS_BYTES;
 static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
 
 namespace {
-
 constexpr int kMaxDevices = 64;
+}  // namespace
+
+namespace moe {
 // 0 = unchecked, 1 = gfx950, 2 = other architecture
-std::atomic<int> g_arch_state[kMaxDevices];
+static std::atomic<int> g_arch_state[kMaxDevices];
 
 int check_device() {
   int dev = 0;
@@ -39,6 +41,10 @@ int check_device() {
   }
   return st == 1 ? MOE_OK : MOE_EDEVICE;
 }
+
+}  // namespace moe
+
+namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -1,4 +1,4 @@
-// Internal launch interface of the routing, GEMM and combine kernels.
+// Internal launch interface of the routing, GEMM, combine and scan kernels.
 #pragma once
 
 #include "moe_common.h"
@@ -7,6 +7,10 @@ namespace moe {
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
+
+// MOE_OK when the current device is a gfx950 (checked once per device and
+// cached), MOE_EDEVICE otherwise or when the query fails.
+int check_device();
 
 struct RouteBuffers {
   float* logits;         // [T][E]
@@ -56,6 +60,9 @@ hipError_t launch_dequant_packed(int nmat, int N, int K, int gate_up, const uint
                                  uint16_t* out, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups,
                              hipStream_t stream);
+hipError_t launch_gdn_scan(int T, int n_k_heads, int n_v_heads, const uint16_t* q,
+                          const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
+                          const float* state_in, float* state_out, uint16_t* o, hipStream_t stream);
 hipError_t launch_pack(int nmat, int N, int K, int gate_up, const uint8_t* q, const uint16_t* s,
                        const uint16_t* b, uint8_t* out, hipStream_t stream);
 

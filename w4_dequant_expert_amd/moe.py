@@ -24,7 +24,13 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_b
             "moe_route_no_alloc",
             "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
             "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_dequant_packed", "moe_w4_packed_bytes",
-            "moe_w4_pack", "moe_read_probe")
+            "moe_w4_pack", "moe_read_probe", "gdn_scan")
+
+
+class GdnDims(ctypes.Structure):
+    """gdn_dims of include/gdn_scan.h."""
+    _fields_ = [("T", ctypes.c_int32), ("n_k_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32)]
 
 
 class Dims(ctypes.Structure):
@@ -102,6 +108,8 @@ def lib():
         L.moe_w4_pack.restype = ctypes.c_int
         L.moe_w4_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   vp, vp, vp, vp, vp]
+        L.gdn_scan.restype = ctypes.c_int
+        L.gdn_scan.argtypes = [P(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -213,6 +221,12 @@ def moe_w4_packed_bytes(rows: int, K: int) -> int:
 def moe_w4_pack(n: int, rows: int, K: int, gate_up: bool, q, s, b, packed, stream=None):
     _check(lib().moe_w4_pack(n, rows, K, 1 if gate_up else 0, _ptr(q), _ptr(s), _ptr(b),
                              _ptr(packed), _stream(stream)), "moe_w4_pack")
+
+
+def gdn_scan(d: GdnDims, q, k, v, g, beta, state_in, state_out, o, stream=None):
+    """Gated DeltaNet scan of include/gdn_scan.h (device tensors or raw addresses)."""
+    _check(lib().gdn_scan(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                          _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)), "gdn_scan")
 
 
 # --------------------------------------------------------------------- device buffers
