@@ -691,6 +691,23 @@ def cpu_baseline(name, budget_tokens):
                        f"use ({threads} of the host's {host_cpus})")
 
 
+def gdn_cpu_baseline(tokens=256):
+    """The scan's oracle (numpy float64, untuned) on a bounded sample: the first
+    `tokens` tokens of the 2048-token sequence at all 32 value heads."""
+    import oracle
+    from synth import bf16_bits_to_f32, build_gdn_config
+    c = build_gdn_config("gdn_prefill2048", T=tokens)
+    f = [bf16_bits_to_f32(c[n]) for n in ("q", "k", "v")]
+    threads, host_cpus = cpu_share()
+    t0 = time.perf_counter()
+    oracle.gated_delta_scan(*f, c["g"], c["beta"])
+    dt = time.perf_counter() - t0
+    return dict(value=tokens / dt, unit="tokens/s", cores=threads, kind="oracle",
+                host_logical_cpus=host_cpus,
+                sample=f"first {tokens} tokens of the 2048-token sequence, 32 value heads ({dt:.1f} s); "
+                       "numpy's BLAS threads")
+
+
 def cpu_share():
     """(CPUs this process may run on, the host's logical CPUs): the affinity mask,
     bounded by a cgroup CPU quota when one is set."""
@@ -777,6 +794,8 @@ def main():
             "frac_of_stream_ceiling": dec["gemm_frac_of_stream_ceiling"]}
         torch.cuda.empty_cache()
         gd = gdn_leg()
+        if not args.no_cpu:
+            gd["cpu_baseline"] = gdn_cpu_baseline()
         extra["gdn_prefill2048"] = gd
         sib["roofline_gdn_prefill2048"] = {
             "bound": "alu", "kernel": "gdn_scan_kernel", "achieved": gd["tflops"],
