@@ -85,6 +85,18 @@ typedef struct moe_dims {
  * once to nearest-even bfloat16).  Gate/up matrices have N = 2I rows (gate
  * rows 0..I-1, up rows I..2I-1) and K = H; down matrices N = H, K = I.
  *
+ * How each GEMM kernel forms the weights (the same affine map, two roundings):
+ *   - tiles of more than 32 rows (the tall-tile kernels): w = bf16(fma(q, s, b))
+ *     as above, each weight rebuilt in registers;
+ *   - tiles of at most 32 rows, and every call with at most 16 tokens: the
+ *     scale is applied after the product, per group of 64 inputs,
+ *     sum_i a_i (q_i s + b) = s sum_i a_i (128 + q_i) + (b - 128 s) sum_i a_i,
+ *     with bf16(128 + q) exact, so the weight q s + b is used exactly (never
+ *     rounded to bfloat16) and only the float32 sums round.
+ * Which kernel serves a row depends on its block's tile height, so a token's
+ * output bits can depend on the batch it is in; both forms are held to the
+ * same tolerance against the float64 oracle.
+ *
  * The GEMMs read the same bytes permuted into a streaming layout, written
  * once by moe_w4_pack: for every 16-row slice and every 128-input step, one
  * 1152-byte block holding the slice's codes in the order the GPU lanes load
@@ -270,10 +282,10 @@ int moe_combine(const moe_dims *d, const moe_route_out *r, const uint16_t *y_slo
                 void *stream);
 
 /*
- * moe_w4_dequant - expand a canonical-layout [rows][K] matrix to bfloat16 in memory, with
- * the same device reconstruction the GEMMs use.  Diagnostic: it materialises
- * exactly the array the fused GEMMs avoid, for bit-exactness checks and for the
- * unfused comparison [LB, "Prefill: ..."].
+ * moe_w4_dequant - expand a canonical-layout [rows][K] matrix to bfloat16 in memory,
+ * w = bf16(fma(q, s, b)).  Diagnostic: it materialises exactly the array the
+ * fused GEMMs avoid, for bit-exactness checks and for the unfused comparison
+ * [LB, "Prefill: ..."].
  *   q [rows][K/2] (16-byte aligned), s, b [rows][K/64], out [rows][K] (16-byte aligned)
  *   K a positive multiple of 64, rows >= 0.
  */
