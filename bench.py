@@ -251,30 +251,73 @@ def graph_ms(fn, n_inner, replays=5):
     return e0.elapsed_time(e1) / (replays * n_inner)
 
 
-def stream_ceiling(nbytes, copies=40, workgroups=(256, 512, 1024, 2048, 4096)):
+def stream_ceiling(nbytes, copies=40, workgroups=(256, 512, 1024, 2048, 4096), graph=True):
     """The streaming-read ceiling B' for nbytes per launch: moe_read_probe over
-    `copies` distinct buffers (more than the Infinity Cache holds), replayed
-    from a HIP graph like the decode steps; the best launch shape counts.  Also
-    the per-launch time of a one-workgroup probe of 16 bytes (a kernel that
-    does nothing measurable), the graph's fixed cost per kernel node."""
+    `copies` distinct buffers (more than the Infinity Cache holds), the best
+    launch shape counting.  graph=True replays the launches from a HIP graph,
+    like the decode steps; graph=False times back-to-back launches with HIP
+    events on the stream they run on (large single launches, like the
+    prefill GEMMs).  Also the per-launch time of a one-workgroup probe of 16
+    bytes (a kernel that does nothing measurable), the graph's fixed cost per
+    kernel node."""
     import torch
 
     import w4_dequant_expert_amd as moe
     n = (nbytes + 15) // 16 * 16
     bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
     sink = torch.zeros(max(workgroups), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def events_ms(fn, reps=3):
+        for i in range(copies):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            for i in range(copies):
+                fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * copies)
+
+    timer = (lambda fn: graph_ms(fn, copies)) if graph else events_ms
     best = None
     per_wg = {}
     for wg in workgroups:
-        ms = graph_ms(lambda i: moe.moe_read_probe(bufs[i], n, sink, wg), copies)
+        ms = timer(lambda i: moe.moe_read_probe(bufs[i], n, sink, wg, stream))
         per_wg[wg] = round(ms * 1e3, 3)
         if best is None or ms < best[0]:
             best = (ms, wg)
-    empty_ms = graph_ms(lambda i: moe.moe_read_probe(bufs[i], 16, sink, 1), copies)
+    empty_ms = timer(lambda i: moe.moe_read_probe(bufs[i], 16, sink, 1, stream))
     del bufs
     return dict(bytes=n, best_us=round(best[0] * 1e3, 3), workgroups=best[1],
                 gbs=n / (best[0] * 1e-3) / 1e9, us_by_workgroups=per_wg,
-                empty_kernel_us=round(empty_ms * 1e3, 3))
+                empty_kernel_us=round(empty_ms * 1e3, 3),
+                timing="hip graph replay" if graph else "hip events, back-to-back launches")
+
+
+def mfma_ceiling(workgroups=512, iters=4000, reps=3):
+    """The achievable bf16 matrix-core rate P': moe_mfma_probe with the tall
+    GEMM's launch shape (four-wave workgroups, two per CU), timed with HIP
+    events on the stream it runs on; the best of `reps` launches."""
+    import torch
+
+    import w4_dequant_expert_amd as moe
+    sink = torch.zeros(workgroups * 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    moe.moe_mfma_probe(workgroups, 10, sink, stream)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        moe.moe_mfma_probe(workgroups, iters, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    flops = workgroups * 4 * iters * 8 * 32 * 32 * 16 * 2
+    return dict(tflops=flops / (best * 1e-3) / 1e12, ms=best, workgroups=workgroups, iters=iters)
 
 
 def decode_leg(copies=40):
@@ -817,15 +860,26 @@ def main():
             **{k: round(v, 5) for k, v in st2.items()},
             gemm_tflops=tf2, gemm_frac_mfma=tf2 / PEAK_BF16_TFLOPS,
             touched_experts=wk2["touched"], tile_m_max=wl2.tile_m_max)
+        pc = mfma_ceiling()
         sib["roofline_prefill2048_zipf"] = {
             "bound": "mfma", "kernels": "w4_gemm_tall4_kernel<true> + <false> (gate/up, down)",
             "achieved": tf2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tf2 / PEAK_BF16_TFLOPS,
+            "mfma_ceiling_tflops": pc["tflops"], "frac_of_mfma_ceiling": tf2 / pc["tflops"],
             "algorithmic_flops": wk2["flops_gate_up"] + wk2["flops_down"],
             "avg_launch_ms": {"gate_up": st2["gate_up_ms"], "down": st2["down_ms"]}}
         del wl2
         torch.cuda.empty_cache()
 
+    ceil512 = None
+    if not args.no_extra and args.only is None:
+        # B' for the headline GEMM: a plain streaming read of its algorithmic
+        # bytes, four buffers rotating (more than the Infinity Cache holds)
+        wl.step(0)  # the routing of a call fixes the touched experts
+        torch.cuda.synchronize()
+        ceil512 = stream_ceiling(wl.work()["bytes_gate_up"], copies=4,
+                                 workgroups=(1024, 2048, 4096, 8192), graph=False)
+        torch.cuda.empty_cache()
     wall, stages = time_workload(wl, args.steps, args.warmup, overlap=args.overlap)
     work = wl.work()
     ms = wall / args.steps * 1e3
@@ -868,7 +922,10 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_record(),
                      "algorithmic_bytes": work["bytes_gate_up"],
                      "implementation_bytes": {"h_written": work["bytes_h"]},
-                     "avg_launch_ms": stages["gate_up_ms"]},
+                     "avg_launch_ms": stages["gate_up_ms"],
+                     "stream_ceiling": ceil512,
+                     "stream_ceiling_gbs": ceil512["gbs"] if ceil512 else None,
+                     "frac_of_stream_ceiling": achieved / ceil512["gbs"] if ceil512 else None},
         **sib,
         "cpu_baseline": None,
         "extra": extra,

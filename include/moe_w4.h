@@ -315,6 +315,18 @@ int moe_w4_dequant_packed(int32_t n, int32_t rows, int32_t K, int32_t gate_up, c
  */
 int moe_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups, void *stream);
 
+/*
+ * moe_mfma_probe - measurement aid, not part of the layer: `workgroups`
+ * workgroups of four waves (two per SIMD at two workgroups per CU, as the
+ * tall-tile GEMM runs) each issue `iters` rounds of eight independent
+ * v_mfma_f32_32x32x16_bf16 on register operands, and lane 0 of each wave
+ * writes a folded value to sink[4 * workgroups].  Work:
+ * workgroups * 4 * iters * 8 * 32768 flops.  Timing it gives the matrix-core
+ * throughput this launch shape reaches with no memory traffic at all.
+ * 1 <= workgroups <= 2^20, 1 <= iters <= 2^24; MOE_EINVAL otherwise.
+ */
+int moe_mfma_probe(int32_t workgroups, int32_t iters, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,11 @@ hipError_t launch_dequant_packed(int, int, int, int, const uint8_t*, uint16_t*, 
 hipError_t launch_read_probe(const void*, size_t, uint32_t*, int, hipStream_t) {
   ++g_launches; return hipErrorInvalidValue;
 }
+hipError_t launch_mfma_probe(int, int, float*, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
+hipError_t launch_gdn_scan(int, int, int, const uint16_t*, const uint16_t*, const uint16_t*,
+                           const float*, const float*, const float*, float*, uint16_t*, hipStream_t) {
+  ++g_launches; return hipErrorInvalidValue;
+}
 hipError_t launch_pack(int, int, int, int, const uint8_t*, const uint16_t*, const uint16_t*,
                        uint8_t*, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 }  // namespace moe
@@ -200,6 +205,11 @@ int main() {
   CHECK(moe_read_probe(packed, 100, reinterpret_cast<uint32_t*>(ys), 4, nullptr) == MOE_EALIGN);
   CHECK(moe_read_probe(packed, 0, reinterpret_cast<uint32_t*>(ys), 4, nullptr) == MOE_OK);
   CHECK(moe_read_probe(packed, 64, reinterpret_cast<uint32_t*>(ys), 0, nullptr) == MOE_EINVAL);
+
+  CHECK(moe_mfma_probe(0, 10, reinterpret_cast<float*>(ys), nullptr) == MOE_EINVAL);
+  CHECK(moe_mfma_probe(4, 0, reinterpret_cast<float*>(ys), nullptr) == MOE_EINVAL);
+  CHECK(moe_mfma_probe(4, 10, reinterpret_cast<float*>(g_mem + 2), nullptr) == MOE_EALIGN);
+  CHECK(moe_mfma_probe(4, 10, nullptr, nullptr) == MOE_EINVAL);
 
   CHECK(moe::g_launches == 0);
   if (g_fail) {

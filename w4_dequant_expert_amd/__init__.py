@@ -31,6 +31,7 @@ from .moe import (  # noqa: F401
     moe_routed_w4_ffn,
     moe_shared_w4_ffn,
     moe_read_probe,
+    moe_mfma_probe,
     moe_w4_dequant,
     moe_w4_dequant_packed,
     moe_w4_pack,

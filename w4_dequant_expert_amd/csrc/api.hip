@@ -431,4 +431,14 @@ int moe_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t workgr
   return launched(launch_read_probe(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)));
 }
 
+int moe_mfma_probe(int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  if (!sink || workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return MOE_EINVAL;
+  if (!aligned(sink, 4)) return MOE_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return launched(launch_mfma_probe(workgroups, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

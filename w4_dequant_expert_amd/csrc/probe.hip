@@ -1,6 +1,8 @@
-// Bandwidth probe for gfx950: a plain streaming read of a device buffer, the
-// ceiling a weight-streaming kernel of the same size and launch path can
-// reach.  Diagnostic only; nothing in the layer calls it.
+// Probes for gfx950: a plain streaming read of a device buffer (the ceiling a
+// weight-streaming kernel of the same size and launch path can reach) and a
+// loop of independent bf16 matrix instructions (the matrix-core throughput a
+// launch shape reaches with no memory traffic).  Diagnostic only; nothing in
+// the layer calls them.
 #include "route.h"
 
 namespace moe {
@@ -39,6 +41,41 @@ hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int 
   hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(workgroups)),
                      dim3(kProbeThreads), 0, stream, static_cast<const uint4*>(src),
                      static_cast<long long>(bytes / 16), sink);
+  return hipGetLastError();
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Eight independent accumulator chains per wave, so every MFMA issue finds its
+// operands ready; the operands come from the lane index, not memory.
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(static_cast<float>((lane + e) & 7) * 0.125f);
+    b[e] = static_cast<__bf16>(static_cast<float>((lane * 3 + e) & 7) * 0.0625f);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+  if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(256), 0,
+                     stream, iters, sink);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ hipError_t launch_dequant_packed(int nmat, int N, int K, int gate_up, const uint
                                  uint16_t* out, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int workgroups,
                              hipStream_t stream);
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t stream);
 hipError_t launch_gdn_scan(int T, int n_k_heads, int n_v_heads, const uint16_t* q,
                           const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
                           const float* state_in, float* state_out, uint16_t* o, hipStream_t stream);

@@ -24,7 +24,7 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_b
             "moe_route_no_alloc",
             "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
             "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_dequant_packed", "moe_w4_packed_bytes",
-            "moe_w4_pack", "moe_read_probe", "gdn_scan")
+            "moe_w4_pack", "moe_read_probe", "moe_mfma_probe", "gdn_scan")
 
 
 class GdnDims(ctypes.Structure):
@@ -108,6 +108,8 @@ def lib():
         L.moe_w4_pack.restype = ctypes.c_int
         L.moe_w4_pack.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   vp, vp, vp, vp, vp]
+        L.moe_mfma_probe.restype = ctypes.c_int
+        L.moe_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.gdn_scan.restype = ctypes.c_int
         L.gdn_scan.argtypes = [P(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -212,6 +214,10 @@ def moe_w4_dequant_packed(n: int, rows: int, K: int, gate_up: bool, packed, out,
 def moe_read_probe(src, nbytes: int, sink, workgroups: int, stream=None):
     _check(lib().moe_read_probe(_ptr(src), nbytes, _ptr(sink), workgroups, _stream(stream)),
            "moe_read_probe")
+
+
+def moe_mfma_probe(workgroups: int, iters: int, sink, stream=None):
+    _check(lib().moe_mfma_probe(workgroups, iters, _ptr(sink), _stream(stream)), "moe_mfma_probe")
 
 
 def moe_w4_packed_bytes(rows: int, K: int) -> int:
