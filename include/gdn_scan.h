@@ -64,6 +64,26 @@ int gdn_scan(const gdn_dims *d, const uint16_t *q, const uint16_t *k, const uint
              const float *g, const float *beta, const float *state_in, float *state_out,
              uint16_t *o, void *stream);
 
+/*
+ * gdn_scan_chunked - the same scan regrouped over chunks of 32 tokens, on the
+ * matrix cores: per chunk, the part that does not depend on the state (the
+ * chunk's k.k and q.k products, the triangular solve of the delta rule's
+ * writes, the decays) is computed for every chunk in parallel into `ws`;
+ * then one pass over the chunks carries the state on chip and applies each
+ * chunk with four matrix products (the chunkwise form of the Gated DeltaNet
+ * paper, Yang, Kautz, Hatamizadeh, ICLR 2025).  The state never goes through
+ * memory between chunks.  Same arguments, layouts and results as gdn_scan (to
+ * rounding: float32 throughout, outputs rounded once to bfloat16), plus
+ *   ws        device scratch of at least gdn_scan_chunked_ws_bytes(d) bytes,
+ *             256-byte aligned, owned by the caller (may be NULL when that
+ *             size is 0); its contents are overwritten
+ * Returns as gdn_scan, and MOE_EWS when ws_bytes is too small.
+ */
+size_t gdn_scan_chunked_ws_bytes(const gdn_dims *d);  /* 0 for invalid dims */
+int gdn_scan_chunked(const gdn_dims *d, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const float *g, const float *beta, const float *state_in, float *state_out,
+                     uint16_t *o, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,8 +77,12 @@ def f64(bits):
     return bf16_bits_to_f32(np.asarray(bits).view(np.uint16)).astype(np.float64)
 
 
-def run_gpu(c, state=None, in_place=False):
-    """One gdn_scan call; returns (o bits [T][Hv][dv], final state)."""
+METHODS = ("direct", "chunked")
+
+
+def run_gpu(c, state=None, in_place=False, method="direct"):
+    """One gdn_scan (register-resident) or gdn_scan_chunked call; returns
+    (o bits [T][Hv][dv], final state)."""
     sh = c["shape"]
     g = Guarded()
     o = g((sh.T, sh.n_v_heads, sh.dv), torch.int16)
@@ -89,9 +93,15 @@ def run_gpu(c, state=None, in_place=False):
     else:
         s_out = g((sh.n_v_heads, sh.dv, sh.dk), torch.float32)
     d = moe.GdnDims(sh.T, sh.n_k_heads, sh.n_v_heads, sh.dk, sh.dv)
-    moe.gdn_scan(d, dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["g"]), dev(c["beta"]), s_in, s_out,
-                 o if sh.T > 0 else None)
-    g.check(f"gdn T={sh.T}")
+    args = (d, dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["g"]), dev(c["beta"]), s_in, s_out,
+            o if sh.T > 0 else None)
+    if method == "chunked":
+        nbytes = moe.gdn_scan_chunked_ws_bytes(d)
+        ws = g((max(nbytes, 1),), torch.uint8)
+        moe.gdn_scan_chunked(*args, ws if nbytes else None, nbytes)
+    else:
+        moe.gdn_scan(*args)
+    g.check(f"gdn {method} T={sh.T}")
     return o.cpu().numpy().view(np.uint16), s_out.cpu().numpy()
 
 
@@ -117,41 +127,44 @@ def check(label, o_bits, s_gpu, o_ref, s_ref):
     assert snw <= S_TOL, snw
 
 
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("T", [1, 5, 16, 37, 64, 100])
-def test_tiny_shapes_against_oracle(T):
+def test_tiny_shapes_against_oracle(T, method):
     """Two key heads, four value heads (heads not a multiple of eight), T
     covering one token, a ragged run of 16, whole chunks of 32 and a tail."""
-    note(f"case gdn_tiny T={T}")
+    note(f"case gdn_tiny T={T} {method}")
     c = build_gdn_config("gdn_tiny", T=T)
-    o, s = run_gpu(c)
+    o, s = run_gpu(c, method=method)
     o_ref, s_ref = reference(c)
-    check(f"gdn_tiny T={T}", o, s, o_ref, s_ref)
+    check(f"gdn_tiny T={T} {method}", o, s, o_ref, s_ref)
 
 
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("Hk,Hv,T", [(8, 8, 70), (4, 16, 33), (1, 8, 48)])
-def test_head_groupings(Hk, Hv, T):
+def test_head_groupings(Hk, Hv, T, method):
     """Value heads per key head 1, 4 and 8, with head counts that take the
     XCD-grouped workgroup order."""
-    note(f"case gdn heads Hk={Hk} Hv={Hv} T={T}")
+    note(f"case gdn heads Hk={Hk} Hv={Hv} T={T} {method}")
     c = make_gdn_inputs(GdnShape(T=T, n_k_heads=Hk, n_v_heads=Hv), seed=21)
     c["shape"] = GdnShape(T=T, n_k_heads=Hk, n_v_heads=Hv)
-    o, s = run_gpu(c)
+    o, s = run_gpu(c, method=method)
     o_ref, s_ref = reference(c)
-    check(f"gdn Hk={Hk} Hv={Hv} T={T}", o, s, o_ref, s_ref)
+    check(f"gdn Hk={Hk} Hv={Hv} T={T} {method}", o, s, o_ref, s_ref)
 
 
-def test_initial_state_in_place_and_empty():
-    note("case gdn initial state, in place, T=0")
+@pytest.mark.parametrize("method", METHODS)
+def test_initial_state_in_place_and_empty(method):
+    note(f"case gdn initial state, in place, T=0 {method}")
     c = build_gdn_config("gdn_tiny", T=45, with_state=True)
     o_ref, s_ref = reference(c, c["state"])
-    o, s = run_gpu(c, state=c["state"])
-    check("gdn_tiny T=45 with state", o, s, o_ref, s_ref)
-    o2, s2 = run_gpu(c, state=c["state"], in_place=True)
+    o, s = run_gpu(c, state=c["state"], method=method)
+    check(f"gdn_tiny T=45 with state {method}", o, s, o_ref, s_ref)
+    o2, s2 = run_gpu(c, state=c["state"], in_place=True, method=method)
     assert np.array_equal(o2, o) and np.array_equal(s2, s)
     e = build_gdn_config("gdn_tiny", T=0, with_state=True)
-    _, s0 = run_gpu(e, state=c["state"])
+    _, s0 = run_gpu(e, state=c["state"], method=method)
     assert np.array_equal(s0, c["state"])
-    _, z = run_gpu(e)
+    _, z = run_gpu(e, method=method)
     assert not np.any(z)
 
 
@@ -178,11 +191,32 @@ def test_split_sequence_matches_one_call():
     check("gdn_tiny 37 + 63", np.concatenate([oa, ob]), sb, o_ref, s_ref)
 
 
-def test_prefill2048_full_against_oracle():
+def test_chunked_split_at_chunk_boundary_matches_one_call():
+    """The chunked scan splits a sequence at multiples of 32 tokens into the
+    same chunks as one call, so 64 + 36 tokens give the bits of one call over
+    100."""
+    note("case gdn chunked split sequence")
+    c = build_gdn_config("gdn_tiny", T=100)
+    o, s = run_gpu(c, method="chunked")
+    a = build_gdn_config("gdn_tiny", T=64)
+    b = build_gdn_config("gdn_tiny", T=36, t0=64)
+    oa, sa = run_gpu(a, method="chunked")
+    ob, sb = run_gpu(b, state=sa, method="chunked")
+    assert np.array_equal(np.concatenate([oa, ob]), o)
+    assert np.array_equal(sb, s)
+
+
+@pytest.fixture(scope="module")
+def prefill2048_ref():
+    c = build_gdn_config("gdn_prefill2048")
+    return c, reference(c)
+
+
+@pytest.mark.parametrize("method", METHODS)
+def test_prefill2048_full_against_oracle(prefill2048_ref, method):
     """The 2048-token sequence at 16 key and 32 value heads, every output and
     the final state against the oracle."""
-    note("case gdn_prefill2048 full")
-    c = build_gdn_config("gdn_prefill2048")
-    o, s = run_gpu(c)
-    o_ref, s_ref = reference(c)
-    check("gdn_prefill2048", o, s, o_ref, s_ref)
+    note(f"case gdn_prefill2048 full {method}")
+    c, (o_ref, s_ref) = prefill2048_ref
+    o, s = run_gpu(c, method=method)
+    check(f"gdn_prefill2048 {method}", o, s, o_ref, s_ref)

@@ -19,6 +19,8 @@ from .moe import (  # noqa: F401
     STATUS_BLOCK_OVERFLOW,
     STATUS_NAN_LOGIT,
     gdn_scan,
+    gdn_scan_chunked,
+    gdn_scan_chunked_ws_bytes,
     lib,
     make_dims,
     moe_abi_version,

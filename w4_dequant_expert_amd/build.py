@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w4.so")
-SOURCES = ["route.hip", "ffn.hip", "pack.hip", "probe.hip", "gdn.hip", "api.hip"]
+SOURCES = ["route.hip", "ffn.hip", "pack.hip", "probe.hip", "gdn.hip", "gdn_chunked.hip", "api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

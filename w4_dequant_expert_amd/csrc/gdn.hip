@@ -465,27 +465,65 @@ hipError_t launch_gdn_scan(int T, int n_k_heads, int n_v_heads, const uint16_t* 
 
 namespace {
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-}  // namespace
 
-extern "C" int gdn_scan(const gdn_dims* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const float* g, const float* beta, const float* state_in, float* state_out,
-                        uint16_t* o, void* stream) {
+int validate_gdn_dims(const gdn_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->dk != 128 || d->dv != 128) return MOE_EINVAL;
   if (d->T < 0 || d->T > (1 << 24)) return MOE_EINVAL;
   if (d->n_k_heads < 1 || d->n_v_heads < d->n_k_heads || d->n_v_heads > 1024 ||
       d->n_v_heads % d->n_k_heads)
     return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int validate_gdn(const gdn_dims* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const float* g, const float* beta, const float* state_in, const float* state_out,
+                 const uint16_t* o) {
+  int rc = validate_gdn_dims(d);
+  if (rc) return rc;
   if (d->T > 0 && (!q || !k || !v || !g || !beta || !o)) return MOE_EINVAL;
   if ((q && !aligned_to(q, 16)) || (k && !aligned_to(k, 16)) || (v && !aligned_to(v, 16)) ||
       (o && !aligned_to(o, 16)) || (g && !aligned_to(g, 4)) || (beta && !aligned_to(beta, 4)) ||
       (state_in && !aligned_to(state_in, 16)) || (state_out && !aligned_to(state_out, 16)))
     return MOE_EALIGN;
-  if (d->T == 0 && !state_out) return MOE_OK;
-  int rc = moe::check_device();
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" int gdn_scan(const gdn_dims* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* g, const float* beta, const float* state_in, float* state_out,
+                        uint16_t* o, void* stream) {
+  int rc = validate_gdn(d, q, k, v, g, beta, state_in, state_out, o);
   if (rc) return rc;
+  if (d->T == 0 && !state_out) return MOE_OK;
+  if ((rc = moe::check_device())) return rc;
   (void)hipGetLastError();
   const hipError_t e = moe::launch_gdn_scan(d->T, d->n_k_heads, d->n_v_heads, q, k, v, g, beta,
                                             state_in, state_out, o, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+extern "C" size_t gdn_scan_chunked_ws_bytes(const gdn_dims* d) {
+  if (validate_gdn_dims(d)) return 0;
+  return moe::gdn_chunked_ws_bytes(d->T, d->n_v_heads);
+}
+
+extern "C" int gdn_scan_chunked(const gdn_dims* d, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, const float* g, const float* beta,
+                                const float* state_in, float* state_out, uint16_t* o, void* ws,
+                                size_t ws_bytes, void* stream) {
+  int rc = validate_gdn(d, q, k, v, g, beta, state_in, state_out, o);
+  if (rc) return rc;
+  const size_t need = moe::gdn_chunked_ws_bytes(d->T, d->n_v_heads);
+  if (need && !ws) return MOE_EINVAL;
+  if (ws && !aligned_to(ws, 256)) return MOE_EALIGN;
+  if (ws_bytes < need) return MOE_EWS;
+  if (d->T == 0 && !state_out) return MOE_OK;
+  if ((rc = moe::check_device())) return rc;
+  (void)hipGetLastError();
+  const hipError_t e = moe::launch_gdn_scan_chunked(d->T, d->n_k_heads, d->n_v_heads, q, k, v, g,
+                                                    beta, state_in, state_out, o,
+                                                    static_cast<float*>(ws),
+                                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

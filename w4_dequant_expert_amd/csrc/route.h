@@ -64,6 +64,11 @@ hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t
 hipError_t launch_gdn_scan(int T, int n_k_heads, int n_v_heads, const uint16_t* q,
                           const uint16_t* k, const uint16_t* v, const float* g, const float* beta,
                           const float* state_in, float* state_out, uint16_t* o, hipStream_t stream);
+size_t gdn_chunked_ws_bytes(int T, int n_v_heads);
+hipError_t launch_gdn_scan_chunked(int T, int n_k_heads, int n_v_heads, const uint16_t* q,
+                                   const uint16_t* k, const uint16_t* v, const float* g,
+                                   const float* beta, const float* state_in, float* state_out,
+                                   uint16_t* o, float* ws, hipStream_t stream);
 hipError_t launch_pack(int nmat, int N, int K, int gate_up, const uint8_t* q, const uint16_t* s,
                        const uint16_t* b, uint8_t* out, hipStream_t stream);
 

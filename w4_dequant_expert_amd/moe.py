@@ -24,7 +24,8 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_b
             "moe_route_no_alloc",
             "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
             "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_dequant_packed", "moe_w4_packed_bytes",
-            "moe_w4_pack", "moe_read_probe", "moe_mfma_probe", "gdn_scan")
+            "moe_w4_pack", "moe_read_probe", "moe_mfma_probe", "gdn_scan",
+            "gdn_scan_chunked", "gdn_scan_chunked_ws_bytes")
 
 
 class GdnDims(ctypes.Structure):
@@ -110,6 +111,10 @@ def lib():
                                   vp, vp, vp, vp, vp]
         L.moe_mfma_probe.restype = ctypes.c_int
         L.moe_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+        L.gdn_scan_chunked.restype = ctypes.c_int
+        L.gdn_scan_chunked.argtypes = [P(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gdn_scan_chunked_ws_bytes.restype = ctypes.c_size_t
+        L.gdn_scan_chunked_ws_bytes.argtypes = [P(GdnDims)]
         L.gdn_scan.restype = ctypes.c_int
         L.gdn_scan.argtypes = [P(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
@@ -233,6 +238,18 @@ def gdn_scan(d: GdnDims, q, k, v, g, beta, state_in, state_out, o, stream=None):
     """Gated DeltaNet scan of include/gdn_scan.h (device tensors or raw addresses)."""
     _check(lib().gdn_scan(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                           _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)), "gdn_scan")
+
+
+def gdn_scan_chunked_ws_bytes(d: GdnDims) -> int:
+    return lib().gdn_scan_chunked_ws_bytes(ctypes.byref(d))
+
+
+def gdn_scan_chunked(d: GdnDims, q, k, v, g, beta, state_in, state_out, o, ws, ws_bytes: int,
+                     stream=None):
+    """Chunked Gated DeltaNet scan of include/gdn_scan.h."""
+    _check(lib().gdn_scan_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(ws), ws_bytes,
+                                  _stream(stream)), "gdn_scan_chunked")
 
 
 # --------------------------------------------------------------------- device buffers
