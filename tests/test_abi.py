@@ -204,3 +204,32 @@ def test_gdn_scan_validation_codes():
     assert call(good, g=0x40002) == -2
     assert call(GdnDims(0, 2, 4, 128, 128), q=None, k=None, v=None, g=None, b=None, o=None,
                 so=None) == 0
+
+
+def test_gdn_scan_chunked_validation_codes():
+    """The chunked scan: workspace size from the dimensions, and a workspace
+    too small, missing or misaligned is rejected before any launch."""
+    from w4_dequant_expert_amd.moe import GdnDims
+    L = moe.lib()
+    d = GdnDims(100, 2, 4, 128, 128)
+    need = moe.gdn_scan_chunked_ws_bytes(d)
+    # four chunks of 32 tokens for each of four value heads, one 256-byte
+    # aligned record each, holding at least a 32 x 128 and two 32 x 32 float
+    # matrices
+    rec = need // 16
+    assert need % 16 == 0 and rec % 256 == 0 and rec >= (32 * 128 + 2 * 32 * 32) * 4
+    assert moe.gdn_scan_chunked_ws_bytes(GdnDims(64, 2, 4, 128, 128)) == need // 4 * 2
+    assert moe.gdn_scan_chunked_ws_bytes(GdnDims(0, 2, 4, 128, 128)) == 0
+    assert moe.gdn_scan_chunked_ws_bytes(GdnDims(10, 3, 4, 128, 128)) == 0
+    assert L.gdn_scan_chunked_ws_bytes(None) == 0
+    q, k, v, g, b, so, o, ws = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x70000, 0x80000, 0x100000
+
+    def call(dd, ws_=ws, nb=need):
+        return L.gdn_scan_chunked(ctypes.byref(dd), q, k, v, g, b, None, so, o, ws_, nb, None)
+
+    assert call(d, nb=need - 1) == -3
+    assert call(d, ws_=None) == -1
+    assert call(d, ws_=ws + 16) == -2
+    assert call(GdnDims(16, 2, 4, 64, 128)) == -1
+    assert L.gdn_scan_chunked(ctypes.byref(GdnDims(0, 2, 4, 128, 128)), None, None, None, None, None,
+                              None, None, None, None, 0, None) == 0
