@@ -241,7 +241,6 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   // in flight while the token list is gathered.
   SliceOps c0[SW], c1[SW];
   load_codes(0, c0);
-  load_codes(1, c1);
   if (GATE_UP) {
     block_tokens(a, bi, s_tok);
     __syncthreads();
@@ -257,13 +256,16 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     am[p] = (tid >> 4) + p * 4 * WAVES;
-    a_ok[p] = am[p] < rows;
+    // rows past the block load the block's last row again (a line the
+    // workgroup reads anyway) and are zeroed when stored
+    const int mm = min(am[p], rows - 1);
     if (GATE_UP) {
-      const int tok = a_ok[p] ? s_tok[am[p]] : -1;
-      a_ok[p] = tok >= 0;
-      arow[p] = src + static_cast<size_t>(a_ok[p] ? tok : 0) * K;
+      const int tok = s_tok[mm];
+      a_ok[p] = am[p] < rows && tok >= 0;
+      arow[p] = src + static_cast<size_t>(max(tok, 0)) * K;
     } else {
-      arow[p] = src + static_cast<size_t>(row0 + (a_ok[p] ? am[p] : 0)) * K;
+      a_ok[p] = am[p] < rows;
+      arow[p] = src + static_cast<size_t>(row0 + mm) * K;
     }
   }
   typedef uint4 AChunks[NPASS];
@@ -307,8 +309,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
       group_affine(o[sl].sb.x, gs[sl][0], gc[sl][0]);
       group_affine(o[sl].sb.y, gs[sl][1], gc[sl][1]);
     }
-    load_codes(s + 2, o);
-    if (active) {
+    if (active && s < nk) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         bf16x8 bq[SW][2];
@@ -341,6 +342,8 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     }
     store_a(buf ^ 1, ar, s + 1);
     load_a(s + 2, ar);
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(s + 2, o);
     __syncthreads();
   };
 
@@ -348,35 +351,62 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   load_a(0, ar);
   store_a(0, ar, 0);
   load_a(1, ar);
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(1, c1);  // after A of step 1, the order every step keeps
   __syncthreads();
-  for (int s = 0; s < nk; s += 2) {
+  int s = 0;
+  do {  // nk >= 1: no guard in front of the loop, so no load sinks into it
     step(s, c0, 0, ar);
-    if (s + 1 < nk) step(s + 1, c1, 1, ar);
-  }
-  if (!active) return;
+    step(s + 1, c1, 1, ar);  // past the end: loads clamped, no compute
+    s += 2;
+  } while (s < nk);
 
+  // Epilogue through LDS (free after the last step's barrier): each wave
+  // writes its outputs, rounded to bfloat16, into a [tm][OC * SW * WAVES]
+  // tile, and the workgroup then stores whole 16-byte runs of output rows.
+  // A lane's own outputs are one 2-byte column entry per row, which as
+  // global stores cost one memory instruction per 2 bytes.
+  constexpr int OC = GATE_UP ? 8 : 16;  // output columns per slice
+  constexpr int TW = OC * SW * WAVES;   // output columns of the tile
+  constexpr int TP = TW + 8;            // LDS row pitch (bf16): rows 4 apart fall 16 banks apart
+  static_assert(kSmallM * TP <= 2 * kSmallM * kLDA, "the output tile fits the staging buffers");
+  uint16_t* tile = &As[0][0];
+  if (active) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    if (mt >= mtiles) break;
+    for (int mt = 0; mt < 2; ++mt) {
+      if (mt >= mtiles) break;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + (lane >> 4) * 4 + i;
-      const size_t r = static_cast<size_t>(row0 + m);
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + (lane >> 4) * 4 + i;
 #pragma unroll
-      for (int sl = 0; sl < SW; ++sl) {
-        const int c = bi.nt * (SW * WAVES) + wave * SW + sl;
-        const float v = acc[mt][sl][i];
-        if (GATE_UP) {
-          const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
-          if (n < 8 && m < rows && sl_on[sl]) {
-            const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
-            out[r * a.I + c * 8 + n] = f32_to_bf16(hv);
+        for (int sl = 0; sl < SW; ++sl) {
+          const int col = (wave * SW + sl) * OC + n;
+          const float v = acc[mt][sl][i];
+          if (GATE_UP) {
+            const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
+            if (n < 8) {
+              const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+              tile[m * TP + col] = f32_to_bf16(hv);
+            }
+          } else {
+            tile[m * TP + col] = f32_to_bf16(v);
           }
-        } else if (m < rows && sl_on[sl]) {
-          out[r * a.H + c * 16 + n] = f32_to_bf16(v);
         }
       }
     }
+  }
+  __syncthreads();
+  // 8-column runs: the tile's columns past the matrix (a partial last N tile)
+  // and its rows past the block are not stored
+  constexpr int RUNS = TW / 8;
+  const int ldo = GATE_UP ? a.I : a.H;
+  const int col0 = bi.nt * TW;
+  const int ncols = min(TW, (GATE_UP ? a.I : a.H) - col0);
+  for (int idx = tid; idx < rows * RUNS; idx += 64 * WAVES) {
+    const int m = idx / RUNS, run = idx % RUNS;
+    if (run * 8 < ncols)
+      *reinterpret_cast<uint4*>(out + static_cast<size_t>(row0 + m) * ldo + col0 + run * 8) =
+          *reinterpret_cast<const uint4*>(&tile[m * TP + run * 8]);
   }
 }
 
@@ -618,30 +648,56 @@ __device__ __forceinline__ void tall4_block(const GemmArgs& a, const BlockInfo& 
   }
   if (s < nk) step(s, As0, As1, r1);
   wait_vmcnt<0>();  // the last step's spare copies land before the LDS is released
+  lds_barrier();    // and every wave has read its last activations
 
+  // Epilogue through LDS, as in the small-tile kernel: rows 0..63 of the
+  // [tm][TW] bfloat16 output tile go to As0, rows 64..127 to As1, each row's
+  // 16-byte runs XOR-swizzled by bits 2..3 of the row so that the two rows
+  // one write instruction covers (4 apart, 16 banks apart after the swizzle)
+  // do not collide; then the workgroup stores 16-byte runs of output rows.
+  constexpr int OC = GATE_UP ? 8 : 16;     // output columns per slice
+  constexpr int TW = OC * 2 * CT * kT4Waves;
+  constexpr int RUNS = TW / 8;
+  static_assert(64 * TW * 2 <= kTallBuf && RUNS % 16 == 0, "half a tile fits one buffer");
+  auto tile_off = [](int lr, int col) {  // bf16 offset of (row lr of a half, column col)
+    return lr * TW + (((col >> 3) ^ (((lr >> 2) & 3) << 2)) << 3) + (col & 7);
+  };
   const int n16 = lane & 15;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int ctile = c_first + 2 * ct;
     if (ctile >= nslices) break;
-    const int c = ctile + nsl;
+    const int col = (ctile - bi.nt * (2 * CT * kT4Waves) + nsl) * OC + n16;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      uint16_t* half = reinterpret_cast<uint16_t*>(mt < 2 ? As0 : As1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const size_t r = static_cast<size_t>(row0 + m);
+        const int lr = (mt & 1) * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         const float v = acc[ct][mt][i];
         if (GATE_UP) {
           const float u = __shfl_xor(v, 8, 64);  // lane n (mod 16 < 8) holds gate, n + 8 up
-          if (n16 < 8 && m < rows) {
+          if (n16 < 8) {
             const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
-            out[r * a.I + c * 8 + n16] = f32_to_bf16(hv);
+            half[tile_off(lr, col)] = f32_to_bf16(hv);
           }
-        } else if (m < rows) {
-          out[r * a.H + c * 16 + n16] = f32_to_bf16(v);
+        } else {
+          half[tile_off(lr, col)] = f32_to_bf16(v);
         }
       }
+    }
+  }
+  lds_barrier();
+  // 8-column runs; columns past the matrix and rows past the block are not stored
+  const int ldo = GATE_UP ? a.I : a.H;
+  const int col0 = bi.nt * TW;
+  const int ncols = min(TW, ldo - col0);
+  for (int idx = tid; idx < rows * RUNS; idx += kT4Threads) {
+    const int m = idx / RUNS, run = idx % RUNS;
+    if (run * 8 < ncols) {
+      const uint16_t* half = reinterpret_cast<const uint16_t*>(m < 64 ? As0 : As1);
+      *reinterpret_cast<uint4*>(out + static_cast<size_t>(row0 + m) * ldo + col0 + run * 8) =
+          *reinterpret_cast<const uint4*>(&half[tile_off(m & 63, run * 8)]);
     }
   }
 }
