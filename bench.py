@@ -432,6 +432,318 @@ def gdn_leg(reps=20, warmup=5):
                 state_bytes_kept_on_chip=sh.n_v_heads * sh.dv * sh.dk * 4)
 
 
+def small_batch_leg(Ts=(2, 4, 8), copies=40):
+    """Batches of 2..8 tokens (speculative-verification sized): whole layer
+    calls replayed from a HIP graph, a fresh batch and weight copy per call;
+    distinct experts touched and the weight bytes they pull in."""
+    import numpy as np
+    import torch
+
+    from synth import make_tokens
+    out = {}
+    for T in Ts:
+        wl = Workload("decode1", copies, T=T)
+        fresh = [torch.from_numpy(make_tokens(T, 2048, 4, t0=T * i).view(np.int16)).to("cuda")
+                 for i in range(copies)]
+        for i in range(3):
+            wl.step(i, x=fresh[i], overlap=False)
+        step_ms = graph_ms(lambda i: wl.step(i, x=fresh[i], overlap=False), copies)
+        wl.step(0, x=fresh[0], overlap=False)
+        wk = wl.work()
+        gemm_bytes = wk["bytes_gate_up"] + wk["bytes_down"]
+        out[f"T{T}"] = dict(tokens_per_s=T / (step_ms * 1e-3), ms_per_step=round(step_ms, 5),
+                            touched_experts=wk["touched"], gemm_bytes=gemm_bytes,
+                            layer_hbm_gbs=wk["bytes_layer"] / (step_ms * 1e-3) / 1e9)
+        del wl, fresh
+        torch.cuda.empty_cache()
+    return out
+
+
+def host_route_tables(topk_idx, E, k, n_shared, tile_m_max, tile_gran):
+    """The routing steps after top-k (histogram, exclusive scan, stable scatter,
+    block map) computed on the host with numpy, as an engine that brings the
+    selections back to the CPU does: the host-synced side of the routing
+    ablation.  Same rules as the device tables (checked against them)."""
+    import numpy as np
+    T = topk_idx.shape[0]
+    flat = topk_idx.reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    np.cumsum(counts, out=offsets[1:])
+    sorted_slot = np.argsort(flat, kind="stable").astype(np.int32)
+    slot_pos = np.empty_like(sorted_slot)
+    slot_pos[sorted_slot] = np.arange(T * k, dtype=np.int32)
+    blocks = []
+    for g, c, first in [(e, int(counts[e]), int(offsets[e])) for e in range(E)] + \
+            ([(E, T, T * k)] if n_shared else []):
+        if c == 0:
+            continue
+        nb = -(-c // tile_m_max)
+        base, rem = divmod(c, nb)
+        tm = -(-(base + (rem > 0)) // tile_gran) * tile_gran
+        for i in range(nb):
+            rows = base + (i < rem)
+            blocks.append((g, first, rows, tm))
+            first += rows
+    return counts, offsets, sorted_slot, slot_pos, np.array(blocks, dtype=np.int32).reshape(-1, 4)
+
+
+def ablation_leg(copies, steps=30):
+    """The pages' two MoE ablations at 512 tokens, end to end, each against the
+    library's own layer call (moe_route, moe_grouped_w4_ffn, moe_combine:
+    routing on the GPU, reconstruction fused into the grouped GEMMs).
+    - Host-synced routing: the selections (top-k) are copied to the host, the
+      histogram, scan, scatter and block map are built there (numpy), copied
+      back, and the same GEMM and combine kernels run on them.  (moe_route
+      still builds its own tables on the GPU; the host ones replace them.)
+    - Unfused reconstruction: every call expands the packed 4-bit weights of
+      the 257 experts to bfloat16 in memory (moe_w4_dequant_packed, the same
+      reconstruction as the tall GEMM), then runs batched bfloat16 GEMMs on
+      them (torch.bmm over each expert's rows, padded to 32; the shared expert
+      as plain GEMMs), SwiGLU and the weighted combine as tensor operations."""
+    import numpy as np
+    import torch
+
+    import w4_dequant_expert_amd as moe
+    wl = Workload("prefill512", copies)
+    sh = wl.sh
+    L = wl.layer
+    T, E, k, H, I = wl.T, sh.E, sh.k, sh.H, sh.I
+    rt = L.rt
+    idx_host = torch.empty((T, k), dtype=torch.int32, pin_memory=True)
+    tables_ok = []
+
+    def host_synced(i):
+        r, s_, wr = wl.copies[i % len(wl.copies)]
+        L.w_router = wr
+        d = L.route(wl.x)
+        idx_host.copy_(rt.topk_idx, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        counts, offsets, ss, sp, blocks = host_route_tables(idx_host.numpy(), E, k, sh.n_shared,
+                                                            wl.tile_m_max, 16)
+        if not tables_ok:  # the host tables are the device's, once checked
+            tables_ok.append(np.array_equal(ss, rt.sorted_slot.cpu().numpy()) and
+                             np.array_equal(blocks, rt.blocks[:len(blocks)].cpu().numpy()))
+        rt.counts.copy_(torch.from_numpy(counts), non_blocking=True)
+        rt.offsets.copy_(torch.from_numpy(offsets), non_blocking=True)
+        rt.sorted_slot.copy_(torch.from_numpy(ss), non_blocking=True)
+        rt.slot_pos.copy_(torch.from_numpy(sp), non_blocking=True)
+        rt.blocks[:len(blocks)].copy_(torch.from_numpy(blocks), non_blocking=True)
+        rt.n_blocks.fill_(len(blocks))
+        L.ffn(d, wl.x, r, s_)
+        L.combine(d, wl.y)
+
+    # unfused: expanded bf16 weights, batched GEMMs over the rows in expert
+    # order, each expert's rows padded to P (every expert has at most P rows at
+    # 512 tokens); the shared expert as plain GEMMs over all tokens.  Every
+    # batched product takes contiguous operands only.
+    base_r, base_s = wl.copies[0][0], wl.copies[0][1]
+    P = 32
+    w_gu = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device="cuda")
+    w_dn = torch.empty((E, H, I), dtype=torch.bfloat16, device="cuda")
+    s_gu = torch.empty((1, 2 * I, H), dtype=torch.bfloat16, device="cuda")
+    s_dn = torch.empty((1, H, I), dtype=torch.bfloat16, device="cuda")
+    xb = wl.x.view(torch.bfloat16)
+    F = torch.nn.functional
+
+    def expand():
+        moe.moe_w4_dequant_packed(E, 2 * I, H, True, base_r.t["gu"], w_gu)
+        moe.moe_w4_dequant_packed(E, H, I, False, base_r.t["dn"], w_dn)
+        moe.moe_w4_dequant_packed(1, 2 * I, H, True, base_s.t["gu"], s_gu)
+        moe.moe_w4_dequant_packed(1, H, I, False, base_s.t["dn"], s_dn)
+
+    def unfused_gemms():
+        expert = torch.repeat_interleave(torch.arange(E, device="cuda"), rt.counts.long(),
+                                         output_size=T * k)
+        pos = torch.arange(T * k, device="cuda") - rt.offsets[:E].long()[expert]
+        pad = expert * P + pos                                          # padded row of each slot row
+        a = torch.zeros((E * P, H), dtype=torch.bfloat16, device="cuda")
+        a[pad] = xb.index_select(0, rt.sorted_slot.long() // k)
+        at = a.view(E, P, H).transpose(1, 2).contiguous()               # [E][H][P]
+        gt = torch.bmm(w_gu, at)                                        # [E][2I][P]
+        ht = (F.silu(gt[:, :I].float()) * gt[:, I:].float()).to(torch.bfloat16).contiguous()
+        yt = torch.bmm(w_dn, ht)                                        # [E][H][P]
+        ys = yt.transpose(1, 2).reshape(E * P, H)[pad]                  # rows in expert order
+        g2 = F.linear(xb, s_gu[0])                                      # shared expert
+        y_sh = F.linear((F.silu(g2[:, :I].float()) * g2[:, I:].float()).to(torch.bfloat16), s_dn[0])
+        sel = ys.index_select(0, rt.slot_pos.long()).view(T, k, H).float()
+        y = (sel * rt.topk_w.unsqueeze(-1)).sum(1) + y_sh.float()
+        return y.to(torch.bfloat16)
+
+    def unfused(i):
+        L.route(wl.x)
+        expand()
+        return unfused_gemms()
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+    # warm the clocks, then alternate the paths
+    for i in range(100):
+        wl.step(i)
+    for i in range(10):
+        host_synced(i)
+    out = {}
+    L.w_router = wl.copies[0][2]
+    wl.step(0)  # the fused call on weight copy 0, then the unfused path on the same inputs
+    torch.cuda.synchronize()
+    assert int(rt.counts.max().item()) <= P
+    yf = wl.y.view(torch.bfloat16).float()
+    y_unf = unfused(0).float()
+    out["unfused_vs_fused_max_rel"] = float(((y_unf - yf).abs().max(1).values /
+                                             yf.abs().max(1).values).max())
+    fused, syn, unf, exp_only = [], [], [], []
+    for _ in range(3):
+        fused.append(timed(wl.step))
+        syn.append(timed(host_synced))
+        unf.append(timed(unfused))
+        exp_only.append(timed(lambda i: expand()))
+    fused_ms, synced_ms = min(fused), min(syn)
+    out.update(
+        fused_layer_ms=round(fused_ms, 5),
+        host_synced_routing_layer_ms=round(synced_ms, 5),
+        gpu_resident_routing_speedup=synced_ms / fused_ms,
+        host_tables_match_device=bool(tables_ok and tables_ok[0]),
+        note="layer calls at 512 tokens, wall clock per call over 30 calls, best of 3 alternated "
+             "passes")
+    unf_ms, exp_ms = min(unf), min(exp_only)
+    out.update(unfused_layer_ms=round(unf_ms, 5), unfused_expand_ms=round(exp_ms, 5),
+               unfused_expanded_bytes=(w_gu.numel() + w_dn.numel() + s_gu.numel() + s_dn.numel()) * 2,
+               fused_dequant_speedup=unf_ms / fused_ms)
+    del wl, w_gu, w_dn, s_gu, s_dn
+    torch.cuda.empty_cache()
+    return out
+
+
+def tile_sweep_leg(copies, steps=100, warmup=50):
+    """The pages' tile-height ablation: whole layer calls at 512 and 2048
+    (Zipf-skewed) tokens for each bound on the block map's tile height."""
+    import torch
+    out = {}
+    for name in ("prefill512", "prefill2048_zipf"):
+        for m in (16, 32, 64, 128):
+            wl = Workload(name, copies, m)
+            wall, _ = time_workload(wl, steps, warmup)
+            out[f"{name}_M{m}"] = round(wl.T * steps / wall, 1)
+            del wl
+            torch.cuda.empty_cache()
+    return out
+
+
+def chunked_leg(copies, reps=3):
+    """Long prompt: 16384 tokens as 8 independent layer calls of 2048 tokens
+    (route, gate/up, down, combine each), timed per chunk with HIP events over
+    `reps` passes; steady state is the median over chunks 2..8 of each chunk's
+    fastest pass.  Temporary device memory per chunk is the layer's scratch
+    (routing tables and workspace, h, y_slots), all allocated once up front;
+    the allocator's peak during the timed passes is reported beside it."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    from synth import CONFIGS, make_tokens
+    cfg = CONFIGS["chunked16384"]
+    chunk, n = cfg["chunk"], cfg["T"] // cfg["chunk"]
+    wl = Workload("chunked16384", copies, T=chunk)
+    xs = [torch.from_numpy(make_tokens(chunk, wl.sh.H, cfg["x_seed"], t0=c * chunk).view(np.int16))
+          .to("cuda") for c in range(n)]
+    for c in range(n):                       # warm-up pass
+        wl.step(c, x=xs[c])
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    ms = [[] for _ in range(n)]
+    for r in range(reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for c in range(n):
+            evs[c][0].record()
+            wl.step(n * (r + 1) + c, x=xs[c])
+            evs[c][1].record()
+        torch.cuda.synchronize()
+        for c in range(n):
+            ms[c].append(evs[c][0].elapsed_time(evs[c][1]))
+    best = [min(v) for v in ms]
+    steady = statistics.median(best[1:])
+    L = wl.layer
+    scratch = [t for t in vars(L.rt).values() if isinstance(t, torch.Tensor)] + [L.h, L.y_slots]
+    temp = sum(t.numel() * t.element_size() for t in scratch)
+    out = dict(tokens_per_s=chunk / (steady * 1e-3), chunk_tokens=chunk, chunks=n,
+               chunk_ms=[round(v, 4) for v in best], steady_chunk_ms=round(steady, 4),
+               temp_bytes_per_chunk=temp,
+               alloc_peak_during_chunks=torch.cuda.max_memory_allocated() - base,
+               weight_copies=copies)
+    del wl, xs
+    return out
+
+
+def traffic_record():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None       # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def _pmc_rows(d, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def write_traffic(fetch_dir, write_dir, calib_bytes):
+    """HBM bytes per launch of the dominant kernel, scaled by the same counters'
+    reading for a plain device copy of calib_bytes (read once, written once)."""
+    rec = {"kernel": DOMINANT, "kernel_source_hash": kernel_source_hash()}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(d, counter)
+        kern = [v for _, n, v in rows if DOMINANT in n]
+        copy = [v for _, n, v in rows if "copyBuffer" in n or "copy" in n.lower()]
+        kib = sorted(kern)[len(kern) // 2]           # median over launches, KiB
+        calib_kib = max(copy)                        # the large calibration copy
+        factor = (calib_bytes / 1024.0) / calib_kib
+        rec[key + "_kib_raw"] = kib
+        rec[key + "_calib_kib_raw"] = calib_kib
+        rec[key + "_scale"] = factor
+        rec[key + "_bytes"] = kib * 1024.0 * factor
+    rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
+def cpu_baseline(name, budget_tokens):
+    """The oracle, untuned, on the host cores: route + layer for a sample of the batch."""
+    import oracle
+    from synth import build_config
+    c = build_config(name, T=budget_tokens)
+    sh = c["shape"]
+    threads, host_cpus = cpu_share()
+    t0 = time.perf_counter()
+    r = oracle.route(c["x"], c["wr"], c["bias"], sh.k, sh.n_shared, 128, 16, nthreads=threads)
+    oracle.moe_layer(c["x"], r["topk_idx"], r["topk_w"], c["routed"], c["shared"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=budget_tokens / dt, unit="tokens/s", cores=threads, kind="oracle",
+                host_logical_cpus=host_cpus,
+                sample=f"first {budget_tokens} tokens of the {name} batch: router, top-k, tables and "
+                       f"float64 layer output ({dt:.1f} s), one oracle thread per CPU this job may "
+                       f"use ({threads} of the host's {host_cpus})")
+
+
 def gdn_cpu_baseline(tokens=256):
     """The scan's oracle (numpy float64, untuned) on a bounded sample: the first
     `tokens` tokens of the 2048-token sequence at all 32 value heads."""
