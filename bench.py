@@ -266,7 +266,7 @@ def stream_ceiling(nbytes, copies=40, workgroups=(256, 512, 1024, 2048, 4096), g
     n = (nbytes + 15) // 16 * 16
     bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
     sink = torch.zeros(max(workgroups), dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.current_stream()  # the events' stream (events mode)
 
     def events_ms(fn, reps=3):
         for i in range(copies):
@@ -285,11 +285,12 @@ def stream_ceiling(nbytes, copies=40, workgroups=(256, 512, 1024, 2048, 4096), g
     best = None
     per_wg = {}
     for wg in workgroups:
-        ms = timer(lambda i: moe.moe_read_probe(bufs[i], n, sink, wg, stream))
+        # the stream current at each call: under graph capture, the capturing one
+        ms = timer(lambda i: moe.moe_read_probe(bufs[i], n, sink, wg, torch.cuda.current_stream()))
         per_wg[wg] = round(ms * 1e3, 3)
         if best is None or ms < best[0]:
             best = (ms, wg)
-    empty_ms = timer(lambda i: moe.moe_read_probe(bufs[i], 16, sink, 1, stream))
+    empty_ms = timer(lambda i: moe.moe_read_probe(bufs[i], 16, sink, 1, torch.cuda.current_stream()))
     del bufs
     return dict(bytes=n, best_us=round(best[0] * 1e3, 3), workgroups=best[1],
                 gbs=n / (best[0] * 1e-3) / 1e9, us_by_workgroups=per_wg,
