@@ -172,19 +172,25 @@ class Workload:
 
 
 TIMING_NOTE = ("tokens_per_s and ms_per_step: wall clock of whole layer calls (route, grouped "
-               "FFN, combine) with no events in between; stage times: per-launch averages of "
-               "back-to-back launches of each stage alone between two HIP events")
+               "FFN, combine) with no events in between, after an untimed pass of the stage "
+               "launches and the warm-up calls; stage times: per-launch averages of back-to-back "
+               "launches of each stage alone between two HIP events, after the timed calls")
 
 
 def time_workload(wl, steps, warmup, fresh_tokens=None, overlap=False):
-    """Wall time of `steps` whole layer calls with no events in between
-    (overlap: the shared expert on a second stream), then the average duration
-    (ms) of each stage's launches -- moe_route, moe_w4_gate_up, moe_w4_down,
-    moe_combine -- from `steps` back-to-back launches of that stage alone
-    between two HIP events on the stream they run on (rotating weight copies;
-    the tables of one routing call)."""
+    """`warmup` untimed and `steps` timed whole layer calls with no events in
+    between (overlap: the shared expert on a second stream), wall clock; then
+    the average duration (ms) of each stage's launches -- moe_route,
+    moe_w4_gate_up, moe_w4_down, moe_combine -- from max(steps, 50)
+    back-to-back launches of that stage alone between two HIP events on the
+    stream they run on (rotating weight copies; the tables of one routing
+    call).  One untimed pass of the stage launches comes first, so that the
+    timed calls run at the clocks the same work settles to, whatever the
+    warm-up count."""
     import torch
     tok = (lambda i: None) if fresh_tokens is None else (lambda i: fresh_tokens[i % len(fresh_tokens)])
+    wl.step(0, x=tok(0), overlap=overlap)  # routing tables for the stage launches
+    stage_times(wl, max(steps, 50))
     for i in range(warmup):
         wl.step(i, x=tok(i), overlap=overlap)
     torch.cuda.synchronize()
@@ -193,7 +199,7 @@ def time_workload(wl, steps, warmup, fresh_tokens=None, overlap=False):
         wl.step(warmup + i, x=tok(warmup + i), overlap=overlap)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, stage_times(wl, steps)
+    return wall, stage_times(wl, max(steps, 50))
 
 
 def stage_times(wl, n):

@@ -58,9 +58,12 @@ struct SliceOps {
   uint2 sb;
 };
 
+// blk is wave-uniform: with an unsigned 32-bit lane offset the loads take
+// the scalar-base form (no 64-bit address arithmetic per lane and step).
 __device__ __forceinline__ void load_slice(const uint8_t* blk, int lane, SliceOps& o) {
-  o.q = *reinterpret_cast<const uint4*>(blk + lane * 16);
-  o.sb = *reinterpret_cast<const uint2*>(blk + kPackScales + (lane & 15) * 8);
+  const uint32_t l = static_cast<uint32_t>(lane);
+  o.q = *reinterpret_cast<const uint4*>(blk + l * 16u);
+  o.sb = *reinterpret_cast<const uint2*>(blk + kPackScales + (l & 15u) * 8u);
 }
 
 // Scale after the product.  Within one input group g of a weight row,
@@ -200,25 +203,134 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 }
 
 // ---------------------------------------------------------------------------
-// Small-tile kernel: blocks of at most 32 rows.  WAVES waves, SW slices
-// each (a workgroup covers SW * WAVES slices of one block); each thread
-// stages 32 * 16 / (64 WAVES) activation chunks per step.
+// Small-tile kernel: blocks of at most 32 rows, MT = 1 or 2 row tiles of 16.
+// WAVES waves, SW slices each (a workgroup covers SW * WAVES slices of one
+// block); each thread stages MT * 16 * 16 / (64 WAVES) activation chunks per
+// step.
+//
+// The folded bias term of the scale-after identity, sum over the groups g of
+// c[n][g] X_g[m] (X_g[m] the sum of row m's activations over group g), is a
+// product over the groups: four groups at a time it is one float32 MFMA
+// (16x16x4: A[m][k] = X_g[m], B[k][n] = c[n][g] for the k-th group of the
+// window), in place of one FMA per output and group.  For that each lane
+// keeps the X and c of one group of every window of four: lane l, l/16 = q,
+// keeps group 4w + q.  X comes from the matrix core transposed (ones times
+// the activation fragment, so lane l receives X_g[l mod 16]), which is
+// already the A layout of the float32 MFMA; c[n][g] is the lane's own
+// column's.  Two steps make one window.
 // ---------------------------------------------------------------------------
 
-template <int WAVES, int SW, bool GATE_UP>
+// One step of the small-tile product for SW slices and MT row tiles: the
+// slices' 128 + q operands, per tile and group the transposed X and the P of
+// each slice on the matrix core, P s into the accumulators and this lane's X
+// and c for its group of the window (wpos: the window place of the step's
+// first group, 0 or 2).  a points at row n, input lk of the step in an
+// activation tile of row pitch `pitch` (bf16).
+template <int SW, int MT>
+__device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const uint16_t* a, int pitch,
+                                                int wpos, int q4, const bf16x8& ones,
+                                                const PairConsts& pk, f32x4 (&acc)[MT][SW],
+                                                float (&xk)[MT], float (&ck)[SW]) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  uint32_t qw[SW][4];
+  float gs[SW][2], gc[SW][2];
+#pragma unroll
+  for (int sl = 0; sl < SW; ++sl) {
+    qw[sl][0] = o[sl].q.x;
+    qw[sl][1] = o[sl].q.y;
+    qw[sl][2] = o[sl].q.z;
+    qw[sl][3] = o[sl].q.w;
+    group_affine(o[sl].sb.x, gs[sl][0], gc[sl][0]);
+    group_affine(o[sl].sb.y, gs[sl][1], gc[sl][1]);
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int wg = wpos + g;  // the group's place in its window
+    bf16x8 bq[SW][2];
+#pragma unroll
+    for (int sl = 0; sl < SW; ++sl) {
+      bq[sl][0] = codes_plus128(qw[sl][2 * g], pk);
+      bq[sl][1] = codes_plus128(qw[sl][2 * g + 1], pk);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* ap = a + mt * 16 * pitch + 64 * g;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 32);
+      f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a0, zero, 0, 0, 0);
+      X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a1, X, 0, 0, 0);
+      // the window's first group clears the other lanes' entries, so a step
+      // that is not computed contributes nothing
+      xk[mt] = (q4 == wg) ? X[0] : (wg == 0 ? 0.0f : xk[mt]);
+#pragma unroll
+      for (int sl = 0; sl < SW; ++sl) {
+        f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq[sl][1], P, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][sl][i] = __builtin_fmaf(P[i], gs[sl][g], acc[mt][sl][i]);
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < SW; ++sl) ck[sl] = (q4 == wg) ? gc[sl][g] : (wg == 0 ? 0.0f : ck[sl]);
+  }
+}
+
+// The window's bias terms, sum over its four groups of X_g[m] c[n][g].
+template <int SW, int MT>
+__device__ __forceinline__ void small_window_bias(f32x4 (&acc)[MT][SW], const float (&xk)[MT],
+                                                  const float (&ck)[SW]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int sl = 0; sl < SW; ++sl)
+      acc[mt][sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(xk[mt], ck[sl], acc[mt][sl], 0, 0, 0);
+}
+
+// Rounds a small-tile workgroup's outputs into the LDS tile (row pitch TP,
+// OC columns per slice; gate/up: SwiGLU first, lane n < 8 holds the gate and
+// n + 8 the up value of column n).
+template <int WAVES, int SW, bool GATE_UP, int MT, int TP>
+__device__ __forceinline__ void small_tile_out(const f32x4 (&acc)[MT][SW], uint16_t* tile, int wave,
+                                               int n, int q4) {
+  constexpr int OC = GATE_UP ? 8 : 16;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + q4 * 4 + i;
+#pragma unroll
+      for (int sl = 0; sl < SW; ++sl) {
+        const int col = (wave * SW + sl) * OC + n;
+        const float v = acc[mt][sl][i];
+        if (GATE_UP) {
+          const float u = __shfl_xor(v, 8, 64);
+          if (n < 8) {
+            const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
+            tile[m * TP + col] = f32_to_bf16(hv);
+          }
+        } else {
+          tile[m * TP + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+template <int WAVES, int SW, bool GATE_UP, int MT>
 __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
                                             uint16_t (*As)[kSmallM * kLDA],
                                             int* s_tok) {
+  static_assert(MT == 1 || MT == 2, "16 or 32 rows");
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int nk = pack_steps(K);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int n = lane & 15;
-  const int lk = (lane >> 4) * 8;
-  const int mtiles = bi.tm >> 4;
+  const int q4 = lane >> 4;
+  const int lk = q4 * 8;
   const int row0 = bi.row0, rows = bi.rows;
 
   bool sl_on[SW];
@@ -237,8 +349,8 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
 #pragma unroll
     for (int sl = 0; sl < SW; ++sl) load_slice(sbase[sl] + off, lane, o[sl]);
   };
-  // The codes of steps 0 and 1 do not depend on the block's tokens: they are
-  // in flight while the token list is gathered.
+  // The codes of step 0 do not depend on the block's tokens: they are in
+  // flight while the token list is gathered.
   SliceOps c0[SW], c1[SW];
   load_codes(0, c0);
   if (GATE_UP) {
@@ -246,9 +358,10 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     __syncthreads();
   }
 
-  // A staging: tm rows x 16 chunks of 16 bytes, NPASS chunks per thread
-  // (rows am, am + 4 WAVES, ...); rows past the block read row 0 and are zeroed
-  constexpr int NPASS = kSmallM * 16 / (64 * WAVES);
+  // A staging: MT*16 rows x 16 chunks of 16 bytes, NPASS chunks per thread
+  // (rows am, am + 4 WAVES, ...)
+  constexpr int NPASS = MT * 16 * 16 / (64 * WAVES);
+  static_assert(NPASS >= 1 && NPASS * 64 * WAVES == MT * 256, "whole passes");
   const int ac = tid & 15;
   int am[NPASS];
   bool a_ok[NPASS];
@@ -279,67 +392,28 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     for (int p = 0; p < NPASS; ++p) {
       uint4 v = ar[p];
       if (!(a_ok[p] && s < nk && s * kKS + ac * 8 < K)) v = make_uint4(0, 0, 0, 0);
-      // am < kSmallM always: unconditional, so no divergent branch disturbs
+      // am < MT * 16 always: unconditional, so no divergent branch disturbs
       // the wait counts of the code prefetch
       *reinterpret_cast<uint4*>(&As[buf][am[p] * kLDA + ac * 8]) = v;
     }
   };
-  f32x4 acc[2][SW];
+  f32x4 acc[MT][SW];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int sl = 0; sl < SW; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float xk[MT], ck[SW];  // this lane's group of the current window of four
 
   // Per step: operands 128 + q of both slices and their groups' affine
-  // terms; per 16-row tile and group, X = sum a over the group and P per
-  // slice, both on the matrix core, then the scale-after update.
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  const bf16x8 ones = bf16_ones();
+  // terms; per 16-row tile and group, P per slice and the transposed X on
+  // the matrix core, then P s into the accumulators and the lane's X and c
+  // kept for the window's bias product.
+  bf16x8 ones = bf16_ones();
+  asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt at every use
   const PairConsts pk = pair_consts();
   auto step = [&](int s, SliceOps (&o)[SW], int buf, AChunks& ar) {
-    // this step's codes leave the prefetch registers before the next load
-    uint32_t qw[SW][4];
-    float gs[SW][2], gc[SW][2];
-#pragma unroll
-    for (int sl = 0; sl < SW; ++sl) {
-      qw[sl][0] = o[sl].q.x;
-      qw[sl][1] = o[sl].q.y;
-      qw[sl][2] = o[sl].q.z;
-      qw[sl][3] = o[sl].q.w;
-      group_affine(o[sl].sb.x, gs[sl][0], gc[sl][0]);
-      group_affine(o[sl].sb.y, gs[sl][1], gc[sl][1]);
-    }
-    if (active && s < nk) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        bf16x8 bq[SW][2];
-#pragma unroll
-        for (int sl = 0; sl < SW; ++sl) {
-          bq[sl][0] = codes_plus128(qw[sl][2 * g], pk);
-          bq[sl][1] = codes_plus128(qw[sl][2 * g + 1], pk);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          if (mt < mtiles) {
-            const uint16_t* ap = &As[buf][(mt * 16 + n) * kLDA + lk + 64 * g];
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 32);
-            // the rows' group sums on the matrix core (a ones operand), in the
-            // accumulator layout of P
-            f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, zero, 0, 0, 0);
-            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, X, 0, 0, 0);
-#pragma unroll
-            for (int sl = 0; sl < SW; ++sl) {
-              f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
-              P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq[sl][1], P, 0, 0, 0);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                acc[mt][sl][i] = __builtin_fmaf(P[i], gs[sl][g], __builtin_fmaf(X[i], gc[sl][g], acc[mt][sl][i]));
-            }
-          }
-        }
-      }
-    }
+    if (active && s < nk)
+      small_step_math<SW, MT>(o, &As[buf][n * kLDA + lk], kLDA, 2 * buf, q4, ones, pk, acc, xk, ck);
     store_a(buf ^ 1, ar, s + 1);
     load_a(s + 2, ar);
     __builtin_amdgcn_sched_barrier(0);
@@ -354,15 +428,20 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   __builtin_amdgcn_sched_barrier(0);
   load_codes(1, c1);  // after A of step 1, the order every step keeps
   __syncthreads();
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xk[mt] = 0.0f;
+#pragma unroll
+  for (int sl = 0; sl < SW; ++sl) ck[sl] = 0.0f;
   int s = 0;
   do {  // nk >= 1: no guard in front of the loop, so no load sinks into it
     step(s, c0, 0, ar);
     step(s + 1, c1, 1, ar);  // past the end: loads clamped, no compute
+    small_window_bias<SW, MT>(acc, xk, ck);
     s += 2;
   } while (s < nk);
 
   // Epilogue through LDS (free after the last step's barrier): each wave
-  // writes its outputs, rounded to bfloat16, into a [tm][OC * SW * WAVES]
+  // writes its outputs, rounded to bfloat16, into a [MT*16][OC * SW * WAVES]
   // tile, and the workgroup then stores whole 16-byte runs of output rows.
   // A lane's own outputs are one 2-byte column entry per row, which as
   // global stores cost one memory instruction per 2 bytes.
@@ -371,30 +450,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   constexpr int TP = TW + 8;            // LDS row pitch (bf16): rows 4 apart fall 16 banks apart
   static_assert(kSmallM * TP <= 2 * kSmallM * kLDA, "the output tile fits the staging buffers");
   uint16_t* tile = &As[0][0];
-  if (active) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      if (mt >= mtiles) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + (lane >> 4) * 4 + i;
-#pragma unroll
-        for (int sl = 0; sl < SW; ++sl) {
-          const int col = (wave * SW + sl) * OC + n;
-          const float v = acc[mt][sl][i];
-          if (GATE_UP) {
-            const float u = __shfl_xor(v, 8, 64);  // lane n (< 8) holds gate, n + 8 the up value
-            if (n < 8) {
-              const float hv = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;  // silu(g) * u
-              tile[m * TP + col] = f32_to_bf16(hv);
-            }
-          } else {
-            tile[m * TP + col] = f32_to_bf16(v);
-          }
-        }
-      }
-    }
-  }
+  if (active) small_tile_out<WAVES, SW, GATE_UP, MT, TP>(acc, tile, wave, n, q4);
   __syncthreads();
   // 8-column runs: the tile's columns past the matrix (a partial last N tile)
   // and its rows past the block are not stored
@@ -410,6 +466,143 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Down GEMM, blocks of at most 32 rows, when I <= 512: the block's whole
+// activation tile (its h rows, every input) fits in LDS.  It is staged once;
+// the workgroup then computes NTW consecutive N tiles, streaming only codes,
+// with no barrier between steps and the codes of the next two steps -- across
+// tile boundaries too -- always in flight.  The per-step product is the
+// small-tile kernel's.
+// ---------------------------------------------------------------------------
+constexpr int kResK = 512;             // largest K (= I) the resident-activation kernel takes
+constexpr int kResLDA = kResK + 8;     // its LDS row pitch (bf16)
+constexpr long long kResTargetWgs = 2048;  // grid size the tile grouping keeps
+constexpr int kResDepth = 2;           // steps of codes in flight per wave (four measured slower)
+
+template <int WAVES, int SW, int MT, int DEPTH>
+__device__ __forceinline__ void down_resident_block(const GemmArgs& a, const BlockInfo& bi, int ntw,
+                                                    const uint16_t* __restrict__ src,
+                                                    uint16_t* __restrict__ out, uint16_t* As,
+                                                    uint16_t* Os) {
+  constexpr int SPT = SW * WAVES;        // slices per N tile
+  constexpr int TW = 16 * SPT;           // output columns per N tile
+  constexpr int TP = TW + 8;             // output tile pitch (bf16)
+  constexpr int RUNS = TW / 8;
+  const int K = a.I;
+  const int nk = pack_steps(K);          // 1..4
+  static_assert(DEPTH == 2 || DEPTH == 4, "steps in flight: whole windows of two");
+  const int nkp = (nk + DEPTH - 1) / DEPTH * DEPTH;  // steps per tile, padded to whole prefetch rounds
+  const int nslices = a.H / 16;
+  const int ntiles = (nslices + SPT - 1) / SPT;
+  const int t0 = bi.nt * ntw, t1 = min(t0 + ntw, ntiles);
+  const int F = (t1 - t0) * nkp;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int n = lane & 15, q4 = lane >> 4, lk = q4 * 8;
+  const int row0 = bi.row0, rows = bi.rows;
+
+  // the block's h rows: MT*16 rows x 64 chunks of 8 inputs; rows past the
+  // block and inputs past K are zeros.  Issued before the first codes, so
+  // that waiting for them leaves the codes in flight.
+  constexpr int NA = MT * 16 * (kResK / 8) / (64 * WAVES);
+  static_assert(NA * 64 * WAVES == MT * 16 * (kResK / 8), "whole passes");
+  const int kc = K / 8;
+  uint4 av[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int idx = tid + i * 64 * WAVES;
+    const int m = idx >> 6, ch = idx & 63;
+    av[i] = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + min(m, rows - 1)) * K +
+                                            min(ch, kc - 1) * 8);
+  }
+  // codes of flattened step f: tile t0 + f / nkp, step f % nkp; padding steps
+  // and steps past the last tile reload a valid block (never used)
+  auto load_codes = [&](int f, SliceOps (&o)[SW]) {
+    const int ff = min(f, F - 1);
+    const int t = t0 + ff / nkp, st = min(ff % nkp, nk - 1);
+#pragma unroll
+    for (int sl = 0; sl < SW; ++sl) {
+      const int c = min(t * SPT + wave * SW + sl, nslices - 1);
+      load_slice(bi.P + (static_cast<size_t>(c) * nk + st) * kPackBlock, lane, o[sl]);
+    }
+  };
+  SliceOps cq[DEPTH][SW];  // the codes of the next DEPTH steps
+  __builtin_amdgcn_sched_barrier(0);  // each step's loads in the order the loop keeps
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    load_codes(d, cq[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int idx = tid + i * 64 * WAVES;
+    const int m = idx >> 6, ch = idx & 63;
+    uint4 w = av[i];
+    if (!(m < rows && ch < kc)) w = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&As[m * kResLDA + ch * 8]) = w;
+  }
+  __syncthreads();
+
+  bf16x8 ones = bf16_ones();
+  asm volatile("" : "+v"(ones));
+  const PairConsts pk = pair_consts();
+  f32x4 acc[MT][SW];
+  float xk[MT], ck[SW];
+  int f = 0;
+  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      xk[mt] = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < SW; ++sl) acc[mt][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int sl = 0; sl < SW; ++sl) ck[sl] = 0.0f;
+    const bool act = t * SPT + wave * SW < nslices;
+    for (int s = 0; s < nkp; s += DEPTH, f += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        if (act && s + d < nk)
+          small_step_math<SW, MT>(cq[d], &As[n * kResLDA + (s + d) * kKS + lk], kResLDA, 2 * (d & 1),
+                                  q4, ones, pk, acc, xk, ck);
+        load_codes(f + d + DEPTH, cq[d]);
+        if (d & 1) small_window_bias<SW, MT>(acc, xk, ck);
+      }
+    }
+    // epilogue of tile t through one of two LDS tiles (the other may still be
+    // read by the previous tile's stores)
+    uint16_t* tile = Os + ((t - t0) & 1) * (kSmallM * TP);
+    if (act) small_tile_out<WAVES, SW, false, MT, TP>(acc, tile, wave, n, q4);
+    __syncthreads();
+    const int col0 = t * TW;
+    const int ncols = min(TW, a.H - col0);
+    constexpr int SR = MT * 16 * RUNS / (64 * WAVES);  // runs per thread (a fixed count)
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+      const int idx = tid + i * 64 * WAVES;
+      const int m = idx / RUNS, run = idx % RUNS;
+      if (m < rows && run * 8 < ncols)
+        *reinterpret_cast<uint4*>(out + static_cast<size_t>(row0 + m) * a.H + col0 + run * 8) =
+            *reinterpret_cast<const uint4*>(&tile[m * TP + run * 8]);
+    }
+  }
+}
+
+template <int WAVES, int SW, int MODE>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3))) void w4_down_resident_kernel(
+    GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out, int ntw) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[kSmallM * kResLDA];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[2 * kSmallM * (16 * SW * WAVES + 8)];
+  BlockInfo bi;
+  if (!block_info<false>(a, bi, SW * WAVES * ntw)) return;
+  if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
+  if (!block_valid<false>(a, bi, kSmallM)) return;
+  if (bi.tm <= 16)
+    down_resident_block<WAVES, SW, 1, kResDepth>(a, bi, ntw, src, out, As, Os);
+  else
+    down_resident_block<WAVES, SW, 2, kResDepth>(a, bi, ntw, src, out, As, Os);
+}
+
 // MODE: the blocks the launch computes (GemmArgs::shared_mode: 0 all, 1 the
 // routed ones, 2 the shared expert's), a kernel of its own per mode so that
 // traces tell the launches apart.
@@ -423,7 +616,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
   if (!block_info<GATE_UP>(a, bi, SW * WAVES)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
-  small_block<WAVES, SW, GATE_UP>(a, bi, src, out, As, s_tok);
+  if (bi.tm <= 16)
+    small_block<WAVES, SW, GATE_UP, 1>(a, bi, src, out, As, s_tok);
+  else
+    small_block<WAVES, SW, GATE_UP, 2>(a, bi, src, out, As, s_tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -1161,6 +1357,25 @@ int gemm_m_max_for(int tile_m_max) {
   return tile_m_max <= kSmallM ? 0 : tile_m_max <= kTallM ? kTallM : kTall8M;
 }
 
+// N tiles per workgroup of the resident-activation down kernel: whole tiles,
+// enough of them that the block's staging is amortised, few enough that the
+// grid still holds about two workgroups per slot (three per CU).
+static int down_resident_ntw(const GemmArgs& a, long long blocks8) {
+  const int ntiles = n_tiles<false>(a, kSmallSlices * kSmallWaves);
+  int ntw = 1;
+  while (ntw * 2 <= ntiles && blocks8 * ((ntiles + 2 * ntw - 1) / (2 * ntw)) >= kResTargetWgs) ntw *= 2;
+  return ntw;
+}
+
+template <int MODE>
+static void launch_down_resident(const GemmArgs& a, long long blocks8, const uint16_t* src,
+                                 uint16_t* out, hipStream_t stream) {
+  const int ntw = down_resident_ntw(a, blocks8);
+  const dim3 grid(static_cast<unsigned>(blocks8 * n_tiles<false>(a, kSmallSlices * kSmallWaves * ntw)));
+  hipLaunchKernelGGL((w4_down_resident_kernel<kSmallWaves, kSmallSlices, MODE>), grid,
+                     dim3(64 * kSmallWaves), 0, stream, a, src, out, ntw);
+}
+
 template <bool GATE_UP>
 static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src, uint16_t* out,
                               hipStream_t stream) {
@@ -1177,7 +1392,9 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
     if (nsh <= 0) return hipSuccess;
     const int tm = ((a.T + nsh - 1) / nsh + a.tile_gran - 1) / a.tile_gran * a.tile_gran;
     const long long b8 = (nsh + kXcds - 1) / kXcds * kXcds;
-    if (tm <= kSmallM && !ga.tall_all) {
+    if (tm <= kSmallM && !ga.tall_all && !GATE_UP && a.I <= kResK) {
+      launch_down_resident<2>(ga, b8, src, out, stream);
+    } else if (tm <= kSmallM && !ga.tall_all) {
       hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 2>),
                          dim3(static_cast<unsigned>(b8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves))),
                          dim3(64 * kSmallWaves), 0, stream, ga, src, out);
@@ -1196,7 +1413,12 @@ static hipError_t launch_gemm(const GemmArgs& a, int m_max, const uint16_t* src,
   if (nb <= 0) return hipSuccess;
   const long long blocks8 = (nb + kXcds - 1) / kXcds * kXcds;
   const bool routed_only = a.shared_mode == 1;
-  if (!ga.tall_all) {
+  if (!ga.tall_all && !GATE_UP && a.I <= kResK) {
+    if (routed_only)
+      launch_down_resident<1>(ga, blocks8, src, out, stream);
+    else
+      launch_down_resident<0>(ga, blocks8, src, out, stream);
+  } else if (!ga.tall_all) {
     const dim3 grid_small(static_cast<unsigned>(blocks8 * n_tiles<GATE_UP>(a, kSmallSlices * kSmallWaves)));
     if (routed_only)
       hipLaunchKernelGGL((w4_gemm_small_kernel<kSmallWaves, kSmallSlices, GATE_UP, 1>), grid_small,
