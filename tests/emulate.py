@@ -60,8 +60,8 @@ def exact_weights_per_block(T, k, E, tile_m_max, blocks) -> np.ndarray:
     blocks = np.asarray(blocks).reshape(-1, 4)
     if T <= SHORT_BATCH:
         return np.ones(len(blocks), dtype=bool)
-    if tile_m_max > SMALL_TILE and T * k >= SMALL_TILE * E:   # the tall kernel takes every block
-        return np.zeros(len(blocks), dtype=bool)
+    # blocks of at most 32 rows take the scale-after product in whichever
+    # kernel serves them (the tall-tile kernel too, when it takes every block)
     return blocks[:, 3] <= SMALL_TILE
 
 

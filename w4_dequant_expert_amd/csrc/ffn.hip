@@ -909,6 +909,27 @@ __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* _
   if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
   if (bi.tm > kTallM) return;  // a block of more than 128 rows: the 256-row kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kTallM)) return;
+  if (bi.tm <= kSmallM) {
+    // A short block in a launch that takes every block: the small-tile
+    // product (scale after the product), whose cost per weight does not
+    // depend on the tile height, over the workgroup's 16 slices as two
+    // 8-slice halves.  Rebuilding weights for a single 32-row tile would cost
+    // as much vector work as for four.
+    uint16_t (*As)[kSmallM * kLDA] = reinterpret_cast<uint16_t (*)[kSmallM * kLDA]>(As0);
+    static_assert(2 * kSmallM * kLDA * 2 <= kTallBuf, "the small-tile buffers fit");
+    static_assert(2 * kT4CT * kT4Waves == 2 * kSmallSlices * kSmallWaves && kT4Waves == kSmallWaves,
+                  "a tall workgroup's slices are two small-tile halves");
+    for (int p = 0; p < 2; ++p) {
+      BlockInfo half = bi;
+      half.nt = 2 * bi.nt + p;
+      if (p) __syncthreads();  // the first half's output tile has been stored
+      if (half.tm <= 16)
+        small_block<kSmallWaves, kSmallSlices, GATE_UP, 1>(a, half, src, out, As, s_tok);
+      else
+        small_block<kSmallWaves, kSmallSlices, GATE_UP, 2>(a, half, src, out, As, s_tok);
+    }
+    return;
+  }
   switch ((bi.tm + 31) >> 5) {
     case 1: tall4_block<1, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
     case 2: tall4_block<2, kT4CT, GATE_UP>(a, bi, src, out, As0, As1, s_tok); break;
