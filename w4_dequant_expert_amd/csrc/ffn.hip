@@ -1482,10 +1482,14 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int n
                                                       const uint16_t* __restrict__ y_slots,
                                                       uint16_t* __restrict__ y,
                                                       uint32_t* __restrict__ status) {
+  // one token per workgroup (ceil(H/8 / 256) workgroups per token): the
+  // token's slot positions and weights are workgroup-uniform, scalar loads
   const int chunks = H / 8;
-  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<long long>(T) * chunks) return;
-  const int t = static_cast<int>(idx / chunks), c = static_cast<int>(idx % chunks) * 8;
+  const int cg = (chunks + 255) / 256;
+  const int t = static_cast<int>(blockIdx.x / static_cast<unsigned>(cg));
+  const int ci = static_cast<int>(blockIdx.x % static_cast<unsigned>(cg)) * 256 + static_cast<int>(threadIdx.x);
+  if (t >= T || ci >= chunks) return;
+  const int c = ci * 8;
   const int Sk = T * k;
   // The shared row and, eight slots at a time, the slot positions, weights and
   // rows are loaded with clamped indices before any is used, so each group of
@@ -1546,8 +1550,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int k, int n
 hipError_t launch_combine(int T, int H, int k, int n_shared, const float* topk_w,
                           const int32_t* slot_pos, const uint16_t* y_slots, uint16_t* y,
                           uint32_t* status, hipStream_t stream) {
-  const long long n = static_cast<long long>(T) * (H / 8);
-  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  const long long n = static_cast<long long>(T) * ((H / 8 + 255) / 256);
+  const dim3 grid(static_cast<unsigned>(n));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, T, H, k, n_shared, topk_w,
                      slot_pos, y_slots, y, status);
   return hipGetLastError();
