@@ -625,6 +625,8 @@ def test_routing_batch_sizes(full_banks, T):
     (192, 64, 5, 5, 1, 250, 256),   # 256-row tiles (one block of 250 rows per group), K tails
     (1088, 320, 24, 4, 1, 1000, 256),  # 160..256-row and shorter tiles, K tails in both GEMMs
     (256, 128, 8, 2, 1, 700, 256),  # 175-row groups: five row tiles
+    (256, 640, 12, 2, 1, 40, 32),   # I > 512: the down GEMM's small-tile kernel (no resident rows)
+    (192, 576, 6, 3, 1, 300, 128),  # I > 512 with tall tiles; I % 128 = 64
     (256, 128, 300, 8, 1, 5, 32),   # more than 256 experts, short batch: one-kernel scores, wide top-k
     (256, 128, 300, 8, 1, 64, 32),  # more than 256 experts: tiled scores, wide top-k, scan
     (128, 64, 1024, 4, 1, 5, 16),   # 1024 experts and a shared one: 1025 groups in the block map

@@ -50,6 +50,21 @@ constexpr int kSmallWaves = 4;
 // reads per slice and was slower (gate/up 92 against 79 us at 512 tokens).
 constexpr int kSmallSlices = 2;
 
+// Workgroup barrier for LDS data whose copies the caller has already waited
+// for.  A plain __syncthreads() would also wait for every copy into LDS still
+// in flight (the prefetch of later steps); the asm's memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Raw operands of one step for one 16-row slice: the lane's four code words
 // (word j for MFMA j) and the (scale, bias) dwords of its row for the step's
 // two input groups.
@@ -224,10 +239,11 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 // slices' 128 + q operands, per tile and group the transposed X and the P of
 // each slice on the matrix core, P s into the accumulators and this lane's X
 // and c for its group of the window (wpos: the window place of the step's
-// first group, 0 or 2).  a points at row n, input lk of the step in an
-// activation tile of row pitch `pitch` (bf16).
-template <int SW, int MT>
-__device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const uint16_t* a, int pitch,
+// first group, 0 or 2).  frag(mt, g, h) is the address of this lane's 16
+// bytes of activations for row tile mt, group g of the step and half h (the
+// step's inputs 64 g + 32 h + 8 (lane / 16) .. +7 of row 16 mt + lane % 16).
+template <int SW, int MT, typename Frag>
+__device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const Frag& frag,
                                                 int wpos, int q4, const bf16x8& ones,
                                                 const PairConsts& pk, f32x4 (&acc)[MT][SW],
                                                 float (&xk)[MT], float (&ck)[SW]) {
@@ -254,9 +270,8 @@ __device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const u
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* ap = a + mt * 16 * pitch + 64 * g;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 32);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(frag(mt, g, 0));
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(frag(mt, g, 1));
       f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a0, zero, 0, 0, 0);
       X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a1, X, 0, 0, 0);
       // the window's first group clears the other lanes' entries, so a step
@@ -320,8 +335,7 @@ template <int WAVES, int SW, bool GATE_UP, int MT>
 __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
-                                            uint16_t (*As)[kSmallM * kLDA],
-                                            int* s_tok) {
+                                            uint16_t* As0, uint16_t* As1, int* s_tok) {
   static_assert(MT == 1 || MT == 2, "16 or 32 rows");
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
@@ -358,43 +372,38 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     __syncthreads();
   }
 
-  // A staging: MT*16 rows x 16 chunks of 16 bytes, NPASS chunks per thread
-  // (rows am, am + 4 WAVES, ...)
-  constexpr int NPASS = MT * 16 * 16 / (64 * WAVES);
-  static_assert(NPASS >= 1 && NPASS * 64 * WAVES == MT * 256, "whole passes");
-  const int ac = tid & 15;
-  int am[NPASS];
-  bool a_ok[NPASS];
+  // Activation staging by direct copies into LDS (global_load_lds): each
+  // copy instruction moves four rows (1 KB), lane l's 16 bytes landing at
+  // byte 16 l of it; rows are 256 bytes with their 16-byte chunks XOR-swizzled
+  // by the row (chunk c of row r at c ^ (r mod 16)), so the 16 rows one MFMA
+  // fragment read covers fall in different banks.  Copy p of wave w moves rows
+  // 4 (p WAVES + w) .. +3.  Rows past the block copy the block's last row and
+  // inputs past K copy the row's last inputs: such rows only reach output rows
+  // that are never stored, and inputs past K meet codes with scale and bias 0.
+  constexpr int NPASS = MT * 16 / (4 * WAVES);
+  static_assert(NPASS >= 1 && NPASS * 4 * WAVES == MT * 16, "whole copies");
+  const int pc = lane & 15;
   const uint16_t* arow[NPASS];
+  int alc[NPASS];  // this lane's logical chunk
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
-    am[p] = (tid >> 4) + p * 4 * WAVES;
-    // rows past the block load the block's last row again (a line the
-    // workgroup reads anyway) and are zeroed when stored
-    const int mm = min(am[p], rows - 1);
+    const int r = 4 * (p * WAVES + wave) + (lane >> 4);
+    alc[p] = pc ^ (r & 15);
+    const int mm = min(r, rows - 1);
     if (GATE_UP) {
-      const int tok = s_tok[mm];
-      a_ok[p] = am[p] < rows && tok >= 0;
-      arow[p] = src + static_cast<size_t>(max(tok, 0)) * K;
+      arow[p] = src + static_cast<size_t>(max(s_tok[mm], 0)) * K;
     } else {
-      a_ok[p] = am[p] < rows;
       arow[p] = src + static_cast<size_t>(row0 + mm) * K;
     }
   }
-  typedef uint4 AChunks[NPASS];
-  auto load_a = [&](int s, AChunks& v) {
+  auto issue_a = [&](int s, int buf) {
+    const int s0 = min(s, nk - 1) * kKS;
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
-      v[p] = *reinterpret_cast<const uint4*>(arow[p] + min(s * kKS + ac * 8, K - 8));
-  };
-  auto store_a = [&](int buf, const AChunks& ar, int s) {
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      uint4 v = ar[p];
-      if (!(a_ok[p] && s < nk && s * kKS + ac * 8 < K)) v = make_uint4(0, 0, 0, 0);
-      // am < MT * 16 always: unconditional, so no divergent branch disturbs
-      // the wait counts of the code prefetch
-      *reinterpret_cast<uint4*>(&As[buf][am[p] * kLDA + ac * 8]) = v;
+    {
+      const uint16_t* gp = arow[p] + min(s0 + alc[p] * 8, K - 8);
+      uint8_t* lp = reinterpret_cast<uint8_t*>((buf ? As1 : As0) + (p * WAVES + wave) * 512);
+      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
     }
   };
   f32x4 acc[MT][SW];
@@ -411,31 +420,44 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   bf16x8 ones = bf16_ones();
   asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt at every use
   const PairConsts pk = pair_consts();
-  auto step = [&](int s, SliceOps (&o)[SW], int buf, AChunks& ar) {
-    if (active && s < nk)
-      small_step_math<SW, MT>(o, &As[buf][n * kLDA + lk], kLDA, 2 * buf, q4, ones, pk, acc, xk, ck);
-    store_a(buf ^ 1, ar, s + 1);
-    load_a(s + 2, ar);
+  // Step s: the copies of step s+1 go into the other buffer (read in step
+  // s-1, released by the barrier that ended it); the step's products; the
+  // codes of step s+2 into the registers the products have read; then a wait
+  // for the copies only (the codes stay in flight) and a barrier that does
+  // not drain global loads.
+  auto step = [&](int s, SliceOps (&o)[SW], int buf) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(s + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (active && s < nk) {
+      const uint16_t* tb = buf ? As1 : As0;
+      auto frag = [&](int mt, int g, int hh) {
+        const int r = mt * 16 + n;
+        return tb + r * kKS + (((q4 + 8 * g + 4 * hh) ^ n) << 3);
+      };
+      small_step_math<SW, MT>(o, frag, 2 * buf, q4, ones, pk, acc, xk, ck);
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_codes(s + 2, o);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * SW>();  // the copies of step s+1 (the codes of step s+2 stay in flight)
+    lds_barrier();
   };
 
-  AChunks ar;
-  load_a(0, ar);
-  store_a(0, ar, 0);
-  load_a(1, ar);
+  issue_a(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_codes(1, c1);  // after A of step 1, the order every step keeps
-  __syncthreads();
+  load_codes(1, c1);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<2 * SW>();  // the copies of step 0 (and the codes of step 0)
+  lds_barrier();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) xk[mt] = 0.0f;
 #pragma unroll
   for (int sl = 0; sl < SW; ++sl) ck[sl] = 0.0f;
   int s = 0;
   do {  // nk >= 1: no guard in front of the loop, so no load sinks into it
-    step(s, c0, 0, ar);
-    step(s + 1, c1, 1, ar);  // past the end: loads clamped, no compute
+    step(s, c0, 0);
+    step(s + 1, c1, 1);  // past the end: loads clamped, no compute
     small_window_bias<SW, MT>(acc, xk, ck);
     s += 2;
   } while (s < nk);
@@ -448,8 +470,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   constexpr int OC = GATE_UP ? 8 : 16;  // output columns per slice
   constexpr int TW = OC * SW * WAVES;   // output columns of the tile
   constexpr int TP = TW + 8;            // LDS row pitch (bf16): rows 4 apart fall 16 banks apart
-  static_assert(kSmallM * TP <= 2 * kSmallM * kLDA, "the output tile fits the staging buffers");
-  uint16_t* tile = &As[0][0];
+  uint16_t* tile = As0;  // at least kSmallM * (16 * SW * WAVES + 8) elements
   if (active) small_tile_out<WAVES, SW, GATE_UP, MT, TP>(acc, tile, wave, n, q4);
   __syncthreads();
   // 8-column runs: the tile's columns past the matrix (a partial last N tile)
@@ -562,9 +583,11 @@ __device__ __forceinline__ void down_resident_block(const GemmArgs& a, const Blo
     for (int s = 0; s < nkp; s += DEPTH, f += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        if (act && s + d < nk)
-          small_step_math<SW, MT>(cq[d], &As[n * kResLDA + (s + d) * kKS + lk], kResLDA, 2 * (d & 1),
-                                  q4, ones, pk, acc, xk, ck);
+        if (act && s + d < nk) {
+          const uint16_t* ar = &As[n * kResLDA + (s + d) * kKS + lk];
+          auto frag = [&](int mt, int g, int hh) { return ar + mt * 16 * kResLDA + 64 * g + 32 * hh; };
+          small_step_math<SW, MT>(cq[d], frag, 2 * (d & 1), q4, ones, pk, acc, xk, ck);
+        }
         load_codes(f + d + DEPTH, cq[d]);
         if (d & 1) small_window_bias<SW, MT>(acc, xk, ck);
       }
@@ -609,7 +632,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3)))
 template <int WAVES, int SW, bool GATE_UP, int MODE>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void w4_gemm_small_kernel(
     GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kSmallM * kLDA];
+  // two staging buffers of 32 rows x 128 inputs, distinct arrays so that the
+  // compiler can tell a read of one from a copy into the other; the first
+  // also holds the output tile (32 rows x 136)
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[kSmallM * (kKS + 8)];
+  __shared__ __attribute__((aligned(1024))) uint16_t As1[kSmallM * kKS];
   __shared__ int s_tok[kSmallM];
 
   BlockInfo bi;
@@ -617,9 +644,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
   if (bi.tm <= 16)
-    small_block<WAVES, SW, GATE_UP, 1>(a, bi, src, out, As, s_tok);
+    small_block<WAVES, SW, GATE_UP, 1>(a, bi, src, out, As0, As1, s_tok);
   else
-    small_block<WAVES, SW, GATE_UP, 2>(a, bi, src, out, As, s_tok);
+    small_block<WAVES, SW, GATE_UP, 2>(a, bi, src, out, As0, As1, s_tok);
 }
 
 // ---------------------------------------------------------------------------
@@ -650,21 +677,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 // j of a step (j = 0..7) lane l carries inputs 16j + 8*(l/32) .. +7.  Lane l
 // receives D column l mod 32, rows 8*(i/4) + 4*(l/32) + (i mod 4), i = 0..15.
 // ---------------------------------------------------------------------------
-// Workgroup barrier for LDS data whose copies the caller has already waited
-// for.  A plain __syncthreads() would also wait for every copy into LDS still
-// in flight (the prefetch of later steps); the asm's memory clobber keeps the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N), leaving the other counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 constexpr int kTallM = 128;
 constexpr int kTallBuf = kTallM * kKS * 2;  // bytes of one staged activation step
 
@@ -915,8 +927,7 @@ __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* _
     // depend on the tile height, over the workgroup's 16 slices as two
     // 8-slice halves.  Rebuilding weights for a single 32-row tile would cost
     // as much vector work as for four.
-    uint16_t (*As)[kSmallM * kLDA] = reinterpret_cast<uint16_t (*)[kSmallM * kLDA]>(As0);
-    static_assert(2 * kSmallM * kLDA * 2 <= kTallBuf, "the small-tile buffers fit");
+    static_assert(kSmallM * (kKS + 8) * 2 <= kTallBuf, "the small-tile buffers fit");
     static_assert(2 * kT4CT * kT4Waves == 2 * kSmallSlices * kSmallWaves && kT4Waves == kSmallWaves,
                   "a tall workgroup's slices are two small-tile halves");
     for (int p = 0; p < 2; ++p) {
@@ -924,9 +935,11 @@ __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* _
       half.nt = 2 * bi.nt + p;
       if (p) __syncthreads();  // the first half's output tile has been stored
       if (half.tm <= 16)
-        small_block<kSmallWaves, kSmallSlices, GATE_UP, 1>(a, half, src, out, As, s_tok);
+        small_block<kSmallWaves, kSmallSlices, GATE_UP, 1>(a, half, src, out, reinterpret_cast<uint16_t*>(As0),
+                                                           reinterpret_cast<uint16_t*>(As1), s_tok);
       else
-        small_block<kSmallWaves, kSmallSlices, GATE_UP, 2>(a, half, src, out, As, s_tok);
+        small_block<kSmallWaves, kSmallSlices, GATE_UP, 2>(a, half, src, out, reinterpret_cast<uint16_t*>(As0),
+                                                           reinterpret_cast<uint16_t*>(As1), s_tok);
     }
     return;
   }
