@@ -67,10 +67,16 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernels' sources with comments and whitespace removed,
+    so the stored traffic record survives edits that leave the code alone."""
+    import re
     h = hashlib.sha256()
     for f in ("moe_common.h", "route.h", "ffn.hip"):
-        with open(os.path.join(ROOT, "w4_dequant_expert_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "w4_dequant_expert_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

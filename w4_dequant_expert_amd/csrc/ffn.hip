@@ -9,8 +9,9 @@
 // Work decomposition: one workgroup = one block of the block map x one N tile
 // (a run of 16-row weight slices).  Within it:
 //   - the block's activation rows (gathered through sorted_slot for gate/up,
-//     contiguous h rows for down) are staged in LDS, 128 inputs at a time,
-//     and shared by all waves of the workgroup;
+//     contiguous h rows for down) are staged in LDS, 128 inputs at a time
+//     (all of them at once in the down kernel for I <= 512), and shared by
+//     all waves of the workgroup;
 //   - each wave owns whole 16-row weight slices; a lane loads 16 bytes of
 //     packed codes (four runs of 8 inputs of one weight row) plus the scale
 //     and bias of the step's two groups, and the codes become MFMA B operands
@@ -18,9 +19,11 @@
 //   - codes are prefetched ahead; all loads are unconditional so the
 //     compiler's wait counts stay exact;
 //   - SwiGLU is applied to the gate/up accumulators before h is stored (gate
-//     and up outputs of a column are 8 lanes apart in the packed slices).
-// Three kernels share this scheme: a small-tile kernel (blocks of <= 32 rows,
+//     and up outputs of a column are 8 lanes apart in the packed slices);
+//     outputs leave through an LDS tile as 16-byte runs of rows.
+// Four kernels share this scheme: a small-tile kernel (blocks of <= 32 rows,
 // high occupancy, the scale applied after the product: streaming-bound work),
+// its down variant with the block's activations resident in LDS (I <= 512),
 // a tall-tile kernel (blocks of 48..128 rows, waves holding 128-row
 // accumulators over rebuilt bf16 weights: matrix-unit-bound work) and a
 // short-batch kernel for at most 16 tokens.  The small and tall kernels each
@@ -39,7 +42,6 @@
 
 namespace moe {
 
-constexpr int kLDA = kKS + 8;     // LDS row pitch in bf16 (16-byte pad against bank conflicts)
 constexpr int kSmallM = 32;       // tiles up to this height go to the small-tile kernel
 // Waves (two slices each) per small-tile workgroup.  Four waves give four
 // workgroups per CU at the kernel's register budget, the same sixteen waves
