@@ -804,12 +804,15 @@ __global__ __launch_bounds__(1024) void route_scan_lds_kernel(
   const int shi = static_cast<int>(static_cast<long long>(blockIdx.x + 1) * S / gridDim.x);
 
   // the first scatter round's slot experts, then the whole bitmask
+  // (only the rounds this launch needs: the conditions are uniform, so no
+  // wave issues a load whose every lane would be clamped)
   int ex[kScatterU];
 #pragma unroll
-  for (int u = 0; u < kScatterU; ++u) ex[u] = topk_idx[min(slo + tid + u * 1024, S - 1)];
+  for (int u = 0; u < kScatterU; ++u)
+    ex[u] = (slo + u * 1024 < shi) ? topk_idx[min(slo + tid + u * 1024, S - 1)] : 0;
   uint32_t bv[kScanLoads];
 #pragma unroll
-  for (int u = 0; u < kScanLoads; ++u) bv[u] = bits[min(tid + u * 1024, nw - 1)];
+  for (int u = 0; u < kScanLoads; ++u) bv[u] = (u * 1024 < nw) ? bits[min(tid + u * 1024, nw - 1)] : 0u;
 #pragma unroll
   for (int u = 0; u < kScanLoads; ++u)
     if (tid + u * 1024 < nw) s_bits[tid + u * 1024] = bv[u];
