@@ -10,9 +10,10 @@
 // Three kernels on one stream:
 //   K1 router scores (float32, fixed evaluation order) and clearing of the
 //      token bitmask;
-//   K2 top-k and weights, 16 lanes per token with DPP row reductions; every
-//      selection sets its token's bit in a [token word][expert] bitmask with
-//      an atomic OR (order-independent, hence deterministic);
+//   K2 top-k and weights, one wave per token with DPP and row-swap
+//      reductions; every selection sets its token's bit in a [token word]
+//      [expert] bitmask with an atomic OR (order-independent, hence
+//      deterministic);
 //   K3 one workgroup: per-expert popcount prefixes over the bitmask give the
 //      histogram and every slot's stable rank, then the exclusive scan, the
 //      block map and the scatter.
@@ -384,16 +385,16 @@ __device__ __forceinline__ float score_from_classes(const float* __restrict__ pa
 }
 
 // ---------------------------------------------------------------------------
-// K2: top-k and weights.  A token is served by one 16-lane row of a wave
-// (four tokens per wave); lane r holds the scores of experts r, r+16, r+32...
-// Every score becomes a 64-bit key: an order-preserving image of the float32
-// score in the high word and the complemented expert index in the low word,
-// so that a larger key means a higher score or, between equal scores, a lower
-// expert index (the selection order), and no two keys are equal.  Round j
-// takes each lane's largest key below the previous round's winner and the
-// row maximum of those over four DPP exchanges (row mirror, half-row mirror,
-// quad swaps by 2 and by 1, which pair every lane with every other through
-// the butterfly).  The rounds are branch-free.
+// K2: top-k and weights.  A token is served by one wave; lane l holds the
+// scores of experts l, l+64, l+128...  Every score becomes a 64-bit key: an
+// order-preserving image of the float32 score in the high word and the
+// complemented expert index in the low word, so that a larger key means a
+// higher score or, between equal scores, a lower expert index (the selection
+// order), and no two keys are equal.  Round j takes each lane's largest key
+// below the previous round's winner and the wave maximum of those: four DPP
+// exchanges within each 16-lane row (row mirror, half-row mirror, quad swaps
+// by 2 and by 1, which pair every lane with every other through the
+// butterfly), then the rows pairwise.  The rounds are branch-free.
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
@@ -426,28 +427,56 @@ __device__ __forceinline__ float order_float(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Top-k of token t for one 16-lane row (lane r = lane mod 16): writes the
-// token's indices and weights (t < T) and returns the experts this lane
-// selected (ranks r and r + 16; -1 where the rank is >= k).
-template <int VPL>  // scores per lane: E <= 16 * VPL
-__device__ __forceinline__ void topk_row(int T, int E, int k, const float* __restrict__ logits,
+// The same exchange across the four rows of a wave: lane l and lane l ^ 16
+// (v_permlane16_swap), then l ^ 32 (v_permlane32_swap).  Swapping a register
+// with itself leaves, in every lane, its own value and its partner's in the
+// two results, in some order; max and + do not care which.
+__device__ __forceinline__ uint64_t max_rows16(uint64_t v) {
+  const auto lo = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v >> 32),
+                                                   false, false);
+  const uint64_t a = (static_cast<uint64_t>(hi[0]) << 32) | lo[0];
+  const uint64_t b = (static_cast<uint64_t>(hi[1]) << 32) | lo[1];
+  return a > b ? a : b;
+}
+__device__ __forceinline__ uint64_t max_rows32(uint64_t v) {
+  const auto lo = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v >> 32),
+                                                   false, false);
+  const uint64_t a = (static_cast<uint64_t>(hi[0]) << 32) | lo[0];
+  const uint64_t b = (static_cast<uint64_t>(hi[1]) << 32) | lo[1];
+  return a > b ? a : b;
+}
+__device__ __forceinline__ float sum_rows(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Top-k of token t for one wave (lane l holds the scores of experts l, l+64,
+// ...): writes the token's indices and weights (t < T) and returns the expert
+// this lane selected (rank l; -1 where l >= k).  A round's local maximum is a
+// tree over the lane's VPL keys (depth log2 VPL, not a chain), then the wave
+// maximum over four DPP steps within the rows and two row swaps.
+template <int VPL>  // scores per lane: E <= 64 * VPL
+__device__ __forceinline__ int topk_wave(int T, int E, int k, const float* __restrict__ logits,
                                          int t, int32_t* __restrict__ topk_idx,
-                                         float* __restrict__ topk_w, uint32_t* __restrict__ status,
-                                         int& sel_a, int& sel_b) {
+                                         float* __restrict__ topk_w, uint32_t* __restrict__ status) {
+  static_assert((VPL & (VPL - 1)) == 0, "a power of two");
   const int lane = threadIdx.x & 63;
-  const int r = lane & 15;
   const bool tok_ok = t < T;
-  const int tt = tok_ok ? t : T - 1;  // rows past T work on a real token and store nothing
+  const int tt = tok_ok ? t : T - 1;  // waves past T work on a real token and store nothing
 
   // every load is issued unconditionally (clamped index), all in flight together
   float val[VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) val[v] = logits[static_cast<size_t>(tt) * E + min(r + 16 * v, E - 1)];
+  for (int v = 0; v < VPL; ++v) val[v] = logits[static_cast<size_t>(tt) * E + min(lane + 64 * v, E - 1)];
   bool saw_nan = false;
   uint64_t key[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
-    const int e = r + 16 * v;
+    const int e = lane + 64 * v;
     const float sc = val[v];
     saw_nan |= (e < E) && (sc != sc);
     const float f = (sc == sc) ? sc + 0.0f : -INFINITY;  // NaN ranks as -inf; -0 as +0
@@ -456,61 +485,57 @@ __device__ __forceinline__ void topk_row(int T, int E, int k, const float* __res
   }
 
   uint64_t prev = ~0ull;
-  uint64_t sel0 = 0, sel1 = 0;  // this lane's selections: ranks r and r + 16
+  uint64_t sel = 0;  // this lane's selection: rank lane
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    uint64_t m[VPL];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) best = (key[v] < prev && key[v] > best) ? key[v] : best;
+    for (int v = 0; v < VPL; ++v) m[v] = key[v] < prev ? key[v] : 0ull;
+#pragma unroll
+    for (int w = VPL / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int v = 0; v < w; ++v) m[v] = m[v + w] > m[v] ? m[v + w] : m[v];
+    uint64_t best = m[0];
     best = max_step<kRowMirror>(best);
     best = max_step<kHalfMirror>(best);
     best = max_step<kQuadSwap2>(best);
     best = max_step<kQuadSwap1>(best);
+    best = max_rows16(best);
+    best = max_rows32(best);
     prev = best;
-    sel0 = (j == r) ? best : sel0;
-    sel1 = (j == r + 16) ? best : sel1;
+    sel = (j == lane) ? best : sel;
   }
-  const float sv0 = order_float(static_cast<uint32_t>(sel0 >> 32));
-  const float sv1 = order_float(static_cast<uint32_t>(sel1 >> 32));
-  const int se0 = static_cast<int>(~static_cast<uint32_t>(sel0));
-  const int se1 = static_cast<int>(~static_cast<uint32_t>(sel1));
+  const float sv = order_float(static_cast<uint32_t>(sel >> 32));
+  const int se = static_cast<int>(~static_cast<uint32_t>(sel));
 
   // weights: exp(l_j - l_max) / sum over the selected (the softmax
   // denominator over all experts cancels in the renormalisation)
-  const float top = __int_as_float(__shfl(__float_as_int(sv0), lane & ~15, 64));
-  const float ex0 = (r < k) ? __expf(sv0 - top) : 0.0f;
-  const float ex1 = (r + 16 < k) ? __expf(sv1 - top) : 0.0f;
-  float den = ex0 + ex1;
+  const float top = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sv)));
+  const float ex = (lane < k) ? __expf(sv - top) : 0.0f;
+  float den = ex;
   den = sum_step<kRowMirror>(den);
   den = sum_step<kHalfMirror>(den);
   den = sum_step<kQuadSwap2>(den);
   den = sum_step<kQuadSwap1>(den);
-  sel_a = (tok_ok && r < k) ? se0 : -1;
-  sel_b = (tok_ok && r + 16 < k) ? se1 : -1;
-  if (tok_ok) {
-    if (r < k) {
-      topk_idx[static_cast<size_t>(t) * k + r] = se0;
-      topk_w[static_cast<size_t>(t) * k + r] = ex0 / den;
-    }
-    if (r + 16 < k) {
-      topk_idx[static_cast<size_t>(t) * k + r + 16] = se1;
-      topk_w[static_cast<size_t>(t) * k + r + 16] = ex1 / den;
-    }
+  den = sum_rows(den);
+  if (tok_ok && lane < k) {
+    topk_idx[static_cast<size_t>(t) * k + lane] = se;
+    topk_w[static_cast<size_t>(t) * k + lane] = ex / den;
   }
   if (saw_nan && tok_ok) status_set(status, MOE_STATUS_NAN_LOGIT);
+  return (tok_ok && lane < k) ? se : -1;
 }
 
-template <int VPL>  // scores per lane: E <= 16 * VPL
+template <int VPL>  // scores per lane: E <= 64 * VPL
 __global__ __launch_bounds__(256) void router_topk_kernel(int T, int E, int k,
                                                           const float* __restrict__ logits,
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w,
                                                           uint32_t* __restrict__ bits,
                                                           uint32_t* __restrict__ status) {
-  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
-  int sa, sb;
-  topk_row<VPL>(T, E, k, logits, t, topk_idx, topk_w, status, sa, sb);
-  if (sa >= 0) atomicOr(&bits[static_cast<size_t>(t >> 5) * E + sa], 1u << (t & 31));
-  if (sb >= 0) atomicOr(&bits[static_cast<size_t>(t >> 5) * E + sb], 1u << (t & 31));
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);  // one token per wave
+  if (t >= T) return;  // wave-uniform; the kernel has no barrier
+  const int se = topk_wave<VPL>(T, E, k, logits, t, topk_idx, topk_w, status);
+  if (se >= 0) atomicOr(&bits[static_cast<size_t>(t >> 5) * E + se], 1u << (t & 31));
 }
 
 // ---------------------------------------------------------------------------
@@ -876,7 +901,7 @@ __global__ __launch_bounds__(1024) void route_scan_lds_kernel(
 
 // ---------------------------------------------------------------------------
 // K2+K3 for short batches (T <= 16): one workgroup does the top-k of every
-// token (16 lanes a token), the histogram and ranks from a per-expert token
+// token (one wave a token), the histogram and ranks from a per-expert token
 // bitmask kept in LDS, the scan, the block map and the scatter, with no
 // global round trip in between.
 // ---------------------------------------------------------------------------
@@ -902,17 +927,12 @@ __global__ __launch_bounds__(1024) void route_short_kernel(
     logits[i] = l;
   }
   __syncthreads();
-  if (tid < kShortT * 16) {  // a full row of lanes per token slot, t < T or not
-    const int t = tid >> 4, r = tid & 15;
-    int sa, sb;
-    topk_row<VPL>(T, E, k, s_logit, t, topk_idx, topk_w, status, sa, sb);
-    if (sa >= 0) {
-      s_sel[t * k + r] = sa;
-      atomicOr(&s_bits[sa], 1u << t);
-    }
-    if (sb >= 0) {
-      s_sel[t * k + r + 16] = sb;
-      atomicOr(&s_bits[sb], 1u << t);
+  if ((tid >> 6) < T) {  // one wave per token (wave-uniform): the waves past T only wait
+    const int t = tid >> 6, r = tid & 63;
+    const int se = topk_wave<VPL / 4>(T, E, k, s_logit, t, topk_idx, topk_w, status);
+    if (se >= 0) {
+      s_sel[t * k + r] = se;
+      atomicOr(&s_bits[se], 1u << t);
     }
   }
   __syncthreads();
@@ -981,12 +1001,12 @@ hipError_t launch_route(const moe_dims& d, const uint16_t* x, const float* wr, c
       hipLaunchKernelGGL((router_scores_kernel<2, 2, 4, false>), g1, dim3(256), 0, stream, T,
                          d.H, E, x, wr, bias, rb.logits, rb.bits, nbits, rb.status);
   }
-  const dim3 g2((T + 15) / 16);
+  const dim3 g2((T + 3) / 4);
   if (E <= 256)
-    hipLaunchKernelGGL((router_topk_kernel<16>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
+    hipLaunchKernelGGL((router_topk_kernel<4>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
                        rb.topk_idx, rb.topk_w, rb.bits, rb.status);
   else
-    hipLaunchKernelGGL((router_topk_kernel<64>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
+    hipLaunchKernelGGL((router_topk_kernel<16>), g2, dim3(256), 0, stream, T, E, k, rb.logits,
                        rb.topk_idx, rb.topk_w, rb.bits, rb.status);
   if (static_cast<long long>((T + 31) / 32) * E <= kScanLdsWords) {
     // the scatter spread over up to eight workgroups (one per 2048 slots)
