@@ -113,8 +113,9 @@ class Workload:
         self.done = torch.cuda.Event()
 
     def step(self, i, ev=None, x=None, overlap=False):
-        """One layer call.  Without events: route, the grouped FFN call and
-        the combine on one stream; with overlap, the shared expert's FFN on a
+        """One layer call.  Without events: route, then the FFN and the combine
+        in one library call (down and combine fused for one token), on one
+        stream; with overlap, the shared expert's FFN on a
         second stream, concurrent with routing (it needs no routing tables),
         the routed experts' FFN after routing, and the combine once both are
         done.  With events (the stage breakdown): route, gate/up, down and
@@ -124,10 +125,9 @@ class Workload:
         L = self.layer
         L.w_router = wr
         x = self.x if x is None else x
-        if ev is None and not overlap:  # one stream, the grouped FFN call
+        if ev is None and not overlap:  # one stream: route, then FFN and combine in one call
             d = L.route(x)
-            L.ffn(d, x, r, s)
-            L.combine(d, self.y)
+            L.ffn_combine(d, x, self.y, r, s)
             return
         if ev is None:
             main = torch.cuda.current_stream()

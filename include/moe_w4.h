@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_W4_ABI_VERSION 3
+#define MOE_W4_ABI_VERSION 4
 
 /* Return codes. */
 #define MOE_OK 0
@@ -280,6 +280,19 @@ int moe_routed_w4_ffn(const moe_dims *d, const uint16_t *x, const moe_route_out 
  */
 int moe_combine(const moe_dims *d, const moe_route_out *r, const uint16_t *y_slots, uint16_t *y,
                 void *stream);
+
+/*
+ * moe_w4_ffn_combine - moe_grouped_w4_ffn followed by moe_combine on one
+ * stream, with the same outputs bit for bit (h, y_slots and y).  For a single
+ * token (T = 1, k + n_shared <= 16, I < 1024) the down GEMM and the combine
+ * run as one kernel, which keeps the token's expert outputs on chip between
+ * the two [LB, "Decode: eliminating per-token CPU round trips": chains of
+ * kernels fused so that intermediates stay in registers].  Arguments, layout
+ * and errors as for the two calls together.
+ */
+int moe_w4_ffn_combine(const moe_dims *d, const uint16_t *x, const moe_route_out *r,
+                       const moe_w4_bank *routed, const moe_w4_bank *shared, uint16_t *h,
+                       uint16_t *y_slots, uint16_t *y, void *stream);
 
 /*
  * moe_w4_dequant - expand a canonical-layout [rows][K] matrix to bfloat16 in memory,

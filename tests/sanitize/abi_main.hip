@@ -25,6 +25,11 @@ hipError_t launch_down(const GemmArgs&, int, const uint16_t*, uint16_t*, hipStre
 }
 hipError_t launch_combine(int, int, int, int, const float*, const int32_t*, const uint16_t*,
                           uint16_t*, uint32_t*, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
+bool down_combine_fused(const GemmArgs& a) { return a.T == 1; }
+hipError_t launch_down_combine_one(const GemmArgs&, const float*, const int32_t*, const uint16_t*,
+                                   uint16_t*, uint16_t*, hipStream_t) {
+  ++g_launches; return hipErrorInvalidValue;
+}
 hipError_t launch_dequant(int, int, const uint8_t*, const uint16_t*, const uint16_t*, uint16_t*,
                           hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_dequant_packed(int, int, int, int, const uint8_t*, uint16_t*, hipStream_t) {
@@ -188,6 +193,9 @@ int main() {
   CHECK(moe_combine(&d, nullptr, ys, y, nullptr) == MOE_EINVAL);
   CHECK(moe_combine(&d, &r, ys, y + 1, nullptr) == MOE_EALIGN);
   CHECK(moe_combine(&d0, &r, ys, y, nullptr) == MOE_OK);
+  CHECK(moe_w4_ffn_combine(&d, x, &r, &bank, &bank, h, ys, nullptr, nullptr) == MOE_EINVAL);
+  CHECK(moe_w4_ffn_combine(&d, x, &r, &bank, &bank, h, ys, y + 1, nullptr) == MOE_EALIGN);
+  CHECK(moe_w4_ffn_combine(&d0, x, &r, &bank, &bank, h, ys, y, nullptr) == MOE_OK);
 
   const uint8_t* q = g_mem + 36864;
   const uint16_t* s = reinterpret_cast<const uint16_t*>(g_mem + 40960);

@@ -109,7 +109,13 @@ def test_ffn_and_combine_validation_codes():
     assert L.moe_grouped_w4_ffn(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
                                 ctypes.byref(bank), 0x8000, None, None) == -1
     assert L.moe_combine(ctypes.byref(d), ctypes.byref(out), 0x1000, 0x1001, None) == -2
+    assert L.moe_w4_ffn_combine(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                                ctypes.byref(bank), 0x8000, 0x9000, None, None) == -1   # y missing
+    assert L.moe_w4_ffn_combine(ctypes.byref(d), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                                ctypes.byref(bank), 0x8000, 0x9000, 0xA008, None) == -2
     d0 = full(0)
+    assert L.moe_w4_ffn_combine(ctypes.byref(d0), 0x1000, ctypes.byref(out), ctypes.byref(bank),
+                                ctypes.byref(bank), 0x8000, 0x9000, 0xA000, None) == 0
     assert L.moe_grouped_w4_ffn(ctypes.byref(d0), 0x1000, ctypes.byref(out), ctypes.byref(bank),
                                 ctypes.byref(bank), 0x8000, 0x9000, None) == 0
     assert L.moe_w4_dequant(4, 100, 0x1000, 0x2000, 0x3000, 0x4000, None) == -1

@@ -539,6 +539,69 @@ def test_grouped_ffn_matches_separate_calls(full_banks, T):
     assert torch.equal(layer.y_slots, ys_ref)
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_ffn_combine_matches_separate_calls(full_banks, T):
+    """moe_w4_ffn_combine (at T = 1 the down GEMM and the combine in one
+    kernel) against moe_grouped_w4_ffn followed by moe_combine: h, y_slots and
+    y equal bit for bit over several fresh tokens, status clear."""
+    routed_np, shared_np, routed_dev, shared_dev = full_banks
+    for i in range(3):
+        c = build_config("decode1", T=T, t0=700 + 16 * i, with_weights=False)
+        sh = c["shape"]
+        note(f"case ffn+combine T={T} tokens from {700 + 16 * i}")
+        layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, sh.n_shared, routed_dev, shared_dev, c["wr"],
+                             c["bias"], T_max=T, tile_m_max=32)
+        x = dev(c["x"])
+        y_ref = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
+        d = layer.route(x)
+        layer.ffn(d, x)
+        layer.combine(d, y_ref)
+        torch.cuda.synchronize()
+        h_ref, ys_ref = layer.h.clone(), layer.y_slots.clone()
+        layer.h.zero_()
+        layer.y_slots.zero_()
+        y = torch.zeros_like(y_ref)
+        layer.ffn_combine(d, x, y)
+        torch.cuda.synchronize()
+        assert int(layer.rt.status.item()) == 0
+        assert torch.equal(layer.h, h_ref)
+        assert torch.equal(layer.y_slots, ys_ref)
+        assert torch.equal(y, y_ref)
+
+
+def test_ffn_combine_one_token_small_layer():
+    """The fused batch-1 kernel with few blocks (top-2 of 8 plus a shared
+    expert: three waves a workgroup) and without a shared expert, against
+    the separate calls and the oracle."""
+    for n_shared in (1, 0):
+        c = build_config("tiny16", T=1)
+        sh = c["shape"]
+        note(f"case tiny T=1 n_shared={n_shared}")
+        routed = moe.DeviceBank(c["routed"])
+        shared = moe.DeviceBank(c["shared"]) if n_shared else None
+        layer = moe.MoeLayer(sh.H, sh.I, sh.E, sh.k, n_shared, routed, shared, c["wr"], None, T_max=1,
+                             tile_m_max=32, export_logits=True)
+        x = dev(c["x"])
+        y_ref = torch.empty((1, sh.H), dtype=torch.int16, device="cuda")
+        d = layer.route(x)
+        layer.ffn(d, x)
+        layer.combine(d, y_ref)
+        torch.cuda.synchronize()
+        ys_ref = layer.y_slots.clone()
+        y = torch.zeros_like(y_ref)
+        layer.ffn_combine(d, x, y)
+        torch.cuda.synchronize()
+        assert int(layer.rt.status.item()) == 0
+        assert torch.equal(layer.y_slots, ys_ref)
+        assert torch.equal(y, y_ref)
+        r = oracle.route(c["x"], c["wr"], None, sh.k, n_shared, 32, 16)
+        yref = oracle.moe_layer(c["x"], r["topk_idx"], r["topk_w"], c["routed"],
+                                c["shared"] if n_shared else None)
+        ygpu = bf16_bits_to_f32(y.cpu().numpy().view(np.uint16)).astype(np.float64)
+        err = oracle.relative_error(ygpu, yref)
+        assert err <= 1e-2, err
+
+
 @pytest.mark.parametrize("cfg,T,tile_m_max", [("decode1", 1, 32), ("decode1", 5, 32),
                                                ("decode1", 48, 32), ("prefill512", 512, 32),
                                                ("decode1", 300, 128), ("prefill2048_zipf", 2048, 128),

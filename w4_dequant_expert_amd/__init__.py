@@ -25,6 +25,7 @@ from .moe import (  # noqa: F401
     make_dims,
     moe_abi_version,
     moe_combine,
+    moe_w4_ffn_combine,
     moe_grouped_w4_ffn,
     moe_max_blocks,
     moe_route,

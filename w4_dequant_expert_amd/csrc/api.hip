@@ -365,6 +365,29 @@ int moe_shared_w4_ffn(const moe_dims* d, const uint16_t* x, const moe_w4_bank* s
   return launched(launch_down(a, m_max, h, y_slots, s));
 }
 
+int moe_w4_ffn_combine(const moe_dims* d, const uint16_t* x, const moe_route_out* r,
+                       const moe_w4_bank* routed, const moe_w4_bank* shared, uint16_t* h,
+                       uint16_t* y_slots, uint16_t* y, void* stream) {
+  int rc = validate_ffn_common(d, r, routed, shared);
+  if (rc) return rc;
+  if (!x || !h || !y_slots || !y || !r->topk_w || !r->slot_pos || !r->status) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(y_slots, 16) || !aligned(y, 16) ||
+      !aligned(r->topk_w, 4) || !aligned(r->slot_pos, 4) || !aligned(r->status, 4))
+    return MOE_EALIGN;
+  if (d->T == 0) return MOE_OK;
+  if ((rc = check_device())) return rc;
+  const GemmArgs a = gemm_args(*d, r, routed, shared);
+  const int m_max = gemm_m_max_for(d->tile_m_max);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if ((rc = launched(launch_gate_up(a, m_max, x, h, s)))) return rc;
+  if (down_combine_fused(a))
+    return launched(launch_down_combine_one(a, r->topk_w, r->slot_pos, h, y_slots, y, s));
+  if ((rc = launched(launch_down(a, m_max, h, y_slots, s)))) return rc;
+  return launched(launch_combine(d->T, d->H, d->k, d->n_shared, r->topk_w, r->slot_pos, y_slots, y,
+                                 r->status, s));
+}
+
 int moe_combine(const moe_dims* d, const moe_route_out* r, const uint16_t* y_slots, uint16_t* y,
                 void* stream) {
   int rc = validate_dims(d);

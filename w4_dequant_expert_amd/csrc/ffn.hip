@@ -1205,6 +1205,58 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
 constexpr int kGemvRows = 16;   // rows per block this kernel accepts
 constexpr int kGemvChunk = 4;   // steps whose loads are in flight together
 
+// The short-batch kernel's pieces, shared with the batch-1 down-and-combine
+// kernel: the codes of kGemvChunk steps of one slice (steps past s_end reload
+// the last one), and one chunk's products (steps past s_end and inputs past K
+// multiply zeros; the weights there are finite) with the scale applied after
+// the product, as in the small-tile kernel.
+__device__ __forceinline__ void gemv_load_w(const uint8_t* sbase, int s0, int s_end, int lane,
+                                            SliceOps (&o)[kGemvChunk]) {
+#pragma unroll
+  for (int u = 0; u < kGemvChunk; ++u)
+    load_slice(sbase + static_cast<size_t>(min(s0 + u, max(s_end - 1, 0))) * kPackBlock, lane, o[u]);
+}
+
+__device__ __forceinline__ void gemv_chunk(const uint16_t* arow, int K, int kq, int s0, int s_end,
+                                           const SliceOps (&o)[kGemvChunk], const bf16x8& ones,
+                                           const PairConsts& pk, f32x4& acc) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  uint4 av[kGemvChunk][4];
+#pragma unroll
+  for (int u = 0; u < kGemvChunk; ++u) {
+    const int s = min(s0 + u, s_end - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      av[u][j] = *reinterpret_cast<const uint4*>(arow + min(s * kKS + 32 * j + kq, K - 8));
+  }
+#pragma unroll
+  for (int u = 0; u < kGemvChunk; ++u) {
+    // The mask is opaque to the compiler, so the loads above stay
+    // unconditional and their wait counts exact.
+    const uint32_t qw[4] = {o[u].q.x, o[u].q.y, o[u].q.z, o[u].q.w};
+    float gs[2], gc[2];
+    group_affine(o[u].sb.x, gs[0], gc[0]);
+    group_affine(o[u].sb.y, gs[1], gc[1]);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      bf16x8 am[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * g + jj;
+        uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + 32 * j + kq < K) ? ~0u : 0u;
+        asm("" : "+v"(mk));
+        am[jj] = as_bf16x8(make_uint4(av[u][j].x & mk, av[u][j].y & mk, av[u][j].z & mk, av[u][j].w & mk));
+      }
+      f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[0], ones, zero, 0, 0, 0);
+      X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[1], ones, X, 0, 0, 0);
+      f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[0], codes_plus128(qw[2 * g], pk), zero, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[1], codes_plus128(qw[2 * g + 1], pk), P, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(P[i], gs[g], __builtin_fmaf(X[i], gc[g], acc[i]));
+    }
+  }
+}
+
 // ONE: a single-token batch, where every gate/up row reads x row 0, so the
 // activation loads need not wait for the slot-to-token lookup.
 template <int KS, bool GATE_UP, bool ONE>
@@ -1257,13 +1309,8 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
   const int rr = bi.row0 + min(r, bi.rows - 1);
   int srow = (GATE_UP && !ONE) ? ((rr < Sk) ? a.sorted_slot[rr] : rr) : rr;
 
-  auto load_w = [&](int s0, SliceOps (&o)[kGemvChunk]) {
-#pragma unroll
-    for (int u = 0; u < kGemvChunk; ++u)
-      load_slice(sbase + static_cast<size_t>(min(s0 + u, max(s_end - 1, 0))) * kPackBlock, lane, o[u]);
-  };
   SliceOps o0[kGemvChunk];
-  load_w(s_begin, o0);
+  gemv_load_w(sbase, s_begin, s_end, lane, o0);
 
   if (GATE_UP && ONE) {
     srow = 0;
@@ -1281,53 +1328,14 @@ __global__ __launch_bounds__(256) void w4_gemv_kernel(GemmArgs a, const uint16_t
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const bf16x8 ones = bf16_ones();
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const PairConsts pk = pair_consts();
-  auto chunk = [&](int s0, const SliceOps (&o)[kGemvChunk]) {
-    uint4 av[kGemvChunk][4];
-#pragma unroll
-    for (int u = 0; u < kGemvChunk; ++u) {
-      const int s = min(s0 + u, s_end - 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        av[u][j] = *reinterpret_cast<const uint4*>(arow + min(s * kKS + 32 * j + kq, K - 8));
-    }
-#pragma unroll
-    for (int u = 0; u < kGemvChunk; ++u) {
-      // Steps past the wave's range and inputs past K multiply zeros (the
-      // mask is opaque to the compiler, so the loads above stay unconditional
-      // and their wait counts exact); the weights there are finite.  Scale
-      // after the product, as in the small-tile kernel.
-      const uint32_t qw[4] = {o[u].q.x, o[u].q.y, o[u].q.z, o[u].q.w};
-      float gs[2], gc[2];
-      group_affine(o[u].sb.x, gs[0], gc[0]);
-      group_affine(o[u].sb.y, gs[1], gc[1]);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        bf16x8 am[2];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * g + jj;
-          uint32_t mk = (s0 + u < s_end && (s0 + u) * kKS + 32 * j + kq < K) ? ~0u : 0u;
-          asm("" : "+v"(mk));
-          am[jj] = as_bf16x8(make_uint4(av[u][j].x & mk, av[u][j].y & mk, av[u][j].z & mk, av[u][j].w & mk));
-        }
-        f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[0], ones, zero, 0, 0, 0);
-        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[1], ones, X, 0, 0, 0);
-        f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[0], codes_plus128(qw[2 * g], pk), zero, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[1], codes_plus128(qw[2 * g + 1], pk), P, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(P[i], gs[g], __builtin_fmaf(X[i], gc[g], acc[i]));
-      }
-    }
-  };
   // the first chunk is peeled, so its weight loads (issued above) are not
   // loop-carried and nothing waits for them before the activation loads
-  if (s_begin < s_end) chunk(s_begin, o0);
+  if (s_begin < s_end) gemv_chunk(arow, K, kq, s_begin, s_end, o0, ones, pk, acc);
   for (int s0 = s_begin + kGemvChunk; s0 < s_end; s0 += kGemvChunk) {
     SliceOps o1[kGemvChunk];
-    load_w(s0, o1);
-    chunk(s0, o1);
+    gemv_load_w(sbase, s0, s_end, lane, o1);
+    gemv_chunk(arow, K, kq, s0, s_end, o1, ones, pk, acc);
   }
 
   if (KS > 1) {
@@ -1569,6 +1577,109 @@ hipError_t launch_combine(int T, int H, int k, int n_shared, const float* topk_w
   const dim3 grid(static_cast<unsigned>(n));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, T, H, k, n_shared, topk_w,
                      slot_pos, y_slots, y, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 down GEMM with the combine in its epilogue.  With one token every
+// block of the map holds one row -- the routed slots in expert order, then
+// the shared expert's -- and block b's row is y_slots row b.  A workgroup
+// owns one 16-column slice of the output and gives each block one wave, which
+// runs the short-batch product over all of I (the same steps, in the same
+// order, as the down launch of w4_gemv_kernel with one wave per slice),
+// stores its row of the slice to y_slots rounded to bfloat16 as that launch
+// does, and keeps it in LDS.  Then sixteen lanes combine the slots as
+// combine_kernel does: float32 fused multiply-adds in rank order, the shared
+// expert's row added last, one rounding to bfloat16.  y_slots and y are
+// bit-identical to the two launches; one launch and y_slots' read-back go.
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxBlocks = 16;
+
+__global__ __launch_bounds__(64 * kFusedMaxBlocks) void w4_down_combine_one_kernel(
+    GemmArgs a, const float* __restrict__ topk_w, const int32_t* __restrict__ slot_pos,
+    const uint16_t* __restrict__ h, uint16_t* __restrict__ y_slots, uint16_t* __restrict__ y) {
+  __shared__ float s_ys[kFusedMaxBlocks][16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int c = blockIdx.x;          // 16-column slice of the output
+  const int nb = a.k + a.n_shared;   // blocks of a one-token map (the block size is 64 nb)
+  // the combine's slot positions and weights (thread j: slot j), loaded
+  // first so that the products cover their latency, kept in LDS below
+  __shared__ int s_pos[kFusedMaxBlocks];
+  __shared__ float s_w[kFusedMaxBlocks];
+  int pj = 0;
+  float wj = 0.0f;
+  if (tid < a.k) {
+    pj = slot_pos[tid];
+    wj = topk_w[tid];
+  }
+  {
+    // the entry is loaded together with the map length (wave < nb <= max_blocks)
+    const int4 blk = reinterpret_cast<const int4*>(a.blocks)[wave];
+    const int nblk = min(*a.n_blocks, a.max_blocks);
+    BlockInfo bi;
+    bi.nt = 0;
+    bi.G = blk.x;
+    bi.row0 = blk.y;
+    bi.rows = blk.z;
+    bi.tm = blk.w;
+    if (nblk == nb && bi.rows == 1 && bi.row0 == wave && block_valid<false>(a, bi, 1 << 30)) {
+      const int nk = pack_steps(a.I);
+      const uint8_t* sbase = bi.P + static_cast<size_t>(c) * nk * kPackBlock;
+      const uint16_t* arow = h + static_cast<size_t>(bi.row0) * a.I;
+      const int kq = (lane >> 4) * 8;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const bf16x8 ones = bf16_ones();
+      const PairConsts pk = pair_consts();
+      SliceOps o0[kGemvChunk];
+      gemv_load_w(sbase, 0, nk, lane, o0);
+      gemv_chunk(arow, a.I, kq, 0, nk, o0, ones, pk, acc);
+      for (int s0 = kGemvChunk; s0 < nk; s0 += kGemvChunk) {
+        SliceOps o1[kGemvChunk];
+        gemv_load_w(sbase, s0, nk, lane, o1);
+        gemv_chunk(arow, a.I, kq, s0, nk, o1, ones, pk, acc);
+      }
+      if (lane < 16) {  // MFMA row 0 (the block's row), column lane
+        const uint16_t v = f32_to_bf16(acc[0]);
+        y_slots[static_cast<size_t>(bi.row0) * a.H + c * 16 + lane] = v;
+        s_ys[wave][lane] = bf16_to_f32(v);
+      }
+    } else {
+      if (lane == 0) status_set(a.status, MOE_STATUS_BAD_INDEX);
+      if (lane < 16) s_ys[wave][lane] = 0.0f;
+    }
+  }
+  if (tid < a.k) {
+    s_pos[tid] = pj;
+    s_w[tid] = wj;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float acc = 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+      const int p = s_pos[j];
+      if (p < 0 || p >= a.k) {
+        status_set(a.status, MOE_STATUS_BAD_INDEX);
+        continue;
+      }
+      acc = __builtin_fmaf(s_w[j], s_ys[p][tid], acc);
+    }
+    if (a.n_shared) acc += s_ys[a.k][tid];
+    y[c * 16 + tid] = f32_to_bf16(acc);
+  }
+}
+
+bool down_combine_fused(const GemmArgs& a) {
+  // one token, at most kFusedMaxBlocks blocks, and a down GEMM that the
+  // short-batch launch runs with one wave per slice (fewer than 8 steps)
+  return a.T == 1 && a.k + a.n_shared <= kFusedMaxBlocks && pack_steps(a.I) < 8 && a.H % 16 == 0;
+}
+
+hipError_t launch_down_combine_one(const GemmArgs& a, const float* topk_w, const int32_t* slot_pos,
+                                   const uint16_t* h, uint16_t* y_slots, uint16_t* y,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(w4_down_combine_one_kernel, dim3(static_cast<unsigned>(a.H / 16)),
+                     dim3(64 * (a.k + a.n_shared)), 0, stream, a, topk_w, slot_pos, h, y_slots, y);
   return hipGetLastError();
 }
 

@@ -54,6 +54,11 @@ hipError_t launch_down(const GemmArgs& a, int m_max, const uint16_t* h, uint16_t
 hipError_t launch_combine(int T, int H, int k, int n_shared, const float* topk_w,
                           const int32_t* slot_pos, const uint16_t* y_slots, uint16_t* y,
                           uint32_t* status, hipStream_t stream);
+// Batch 1: the down GEMM and the combine in one launch (when down_combine_fused).
+bool down_combine_fused(const GemmArgs& a);
+hipError_t launch_down_combine_one(const GemmArgs& a, const float* topk_w, const int32_t* slot_pos,
+                                   const uint16_t* h, uint16_t* y_slots, uint16_t* y,
+                                   hipStream_t stream);
 hipError_t launch_dequant(int rows, int K, const uint8_t* q, const uint16_t* s, const uint16_t* b,
                           uint16_t* out, hipStream_t stream);
 hipError_t launch_dequant_packed(int nmat, int N, int K, int gate_up, const uint8_t* packed,

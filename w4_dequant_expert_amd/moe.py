@@ -23,7 +23,8 @@ STATUS_NAN_LOGIT, STATUS_BAD_INDEX, STATUS_BLOCK_OVERFLOW = 1, 2, 4
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_max_blocks", "moe_route_ws_bytes", "moe_route",
             "moe_route_no_alloc",
             "moe_w4_gate_up", "moe_w4_down", "moe_grouped_w4_ffn", "moe_shared_w4_ffn",
-            "moe_routed_w4_ffn", "moe_combine", "moe_w4_dequant", "moe_w4_dequant_packed", "moe_w4_packed_bytes",
+            "moe_routed_w4_ffn", "moe_combine", "moe_w4_ffn_combine", "moe_w4_dequant",
+            "moe_w4_dequant_packed", "moe_w4_packed_bytes",
             "moe_w4_pack", "moe_read_probe", "moe_mfma_probe", "gdn_scan",
             "gdn_scan_chunked", "gdn_scan_chunked_ws_bytes")
 
@@ -97,6 +98,8 @@ def lib():
         L.moe_routed_w4_ffn.argtypes = [P(Dims), vp, P(RouteOut), P(Bank), vp, vp, vp]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [P(Dims), P(RouteOut), vp, vp, vp]
+        L.moe_w4_ffn_combine.restype = ctypes.c_int
+        L.moe_w4_ffn_combine.argtypes = [P(Dims), vp, P(RouteOut), P(Bank), P(Bank), vp, vp, vp, vp]
         L.moe_w4_dequant.restype = ctypes.c_int
         L.moe_w4_dequant.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
         L.moe_w4_dequant_packed.restype = ctypes.c_int
@@ -204,6 +207,13 @@ def moe_routed_w4_ffn(d: Dims, x, out: RouteOut, routed: Bank, h, y_slots, strea
 def moe_combine(d: Dims, out: RouteOut, y_slots, y, stream=None):
     _check(lib().moe_combine(ctypes.byref(d), ctypes.byref(out), _ptr(y_slots), _ptr(y),
                              _stream(stream)), "moe_combine")
+
+
+def moe_w4_ffn_combine(d: Dims, x, out: RouteOut, routed: Bank, shared, h, y_slots, y, stream=None):
+    _check(lib().moe_w4_ffn_combine(ctypes.byref(d), _ptr(x), ctypes.byref(out), ctypes.byref(routed),
+                                    ctypes.byref(shared) if shared is not None else None,
+                                    _ptr(h), _ptr(y_slots), _ptr(y), _stream(stream)),
+           "moe_w4_ffn_combine")
 
 
 def moe_w4_dequant(rows: int, K: int, q, s, b, out, stream=None):
@@ -414,8 +424,15 @@ class MoeLayer:
     def combine(self, d, y, stream=None):
         moe_combine(d, self.rt.c, self.y_slots, y, stream)
 
+    def ffn_combine(self, d, x, y, routed=None, shared=None, stream=None):
+        """gate/up, down and combine in one library call (down and combine
+        fused for a single token)."""
+        r = routed or self.routed
+        s = shared or self.shared
+        moe_w4_ffn_combine(d, x, self.rt.c, r.c, s.c if s is not None else None, self.h,
+                           self.y_slots, y, stream)
+
     def forward(self, x, y, routed=None, shared=None, stream=None):
         d = self.route(x, stream=stream)
-        self.ffn(d, x, routed, shared, stream)
-        self.combine(d, y, stream)
+        self.ffn_combine(d, x, y, routed, shared, stream)
         return y
