@@ -764,6 +764,23 @@ def cpu_baseline(name, budget_tokens):
                        f"use ({threads} of the host's {host_cpus})")
 
 
+def cpu_single_thread():
+    """The oracle on one thread for the tiny 16-token layer and one decode
+    token of the full-shape layer (its own seeded token), route + layer."""
+    import oracle
+    from synth import build_config
+    out = {}
+    for name, T in (("tiny16", None), ("decode1", 1)):
+        c = build_config(name, T=T)
+        sh = c["shape"]
+        t0 = time.perf_counter()
+        r = oracle.route(c["x"], c["wr"], c["bias"], sh.k, sh.n_shared, 128, 16, nthreads=1)
+        oracle.moe_layer(c["x"], r["topk_idx"], r["topk_w"], c["routed"], c["shared"], nthreads=1)
+        dt = time.perf_counter() - t0
+        out[name] = dict(tokens_per_s=c["T"] / dt, tokens=c["T"], seconds=round(dt, 4), threads=1)
+    return out
+
+
 def gdn_cpu_baseline(tokens=256):
     """The scan's oracle (numpy float64, untuned) on a bounded sample: the first
     `tokens` tokens of the 2048-token sequence at all 32 value heads."""
@@ -978,6 +995,7 @@ def main():
     }
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline("prefill512", 512)
+        out["cpu_baseline"]["single_thread"] = cpu_single_thread()
     print(json.dumps(out))
 
 
