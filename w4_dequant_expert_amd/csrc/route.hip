@@ -663,13 +663,18 @@ __device__ void short_tables_wave(int T, int E, int k, int n_shared, int tile_gr
     c[i] = (e < E) ? __popc(s_bits[e]) : 0;
     packed += (c[i] > 0 ? (1 << 16) : 0) + c[i];
   }
+  // inclusive wave scan on DPP: shifts by 1, 2, 4, 8 within each 16-lane
+  // row (lanes shifted in from outside the row read 0), then each row's total
+  // broadcast into the next rows (row_bcast:15 into rows 1 and 3, row_bcast:31
+  // into rows 2 and 3)
   int inc = packed;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += o;
-  }
-  const int tot = __shfl(inc, 63, 64);
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x111, 0xF, 0xF, true);  // row_shr:1
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x112, 0xF, 0xF, true);  // row_shr:2
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x114, 0xF, 0xF, true);  // row_shr:4
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x118, 0xF, 0xF, true);  // row_shr:8
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  inc += __builtin_amdgcn_update_dpp(0, inc, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  const int tot = __builtin_amdgcn_readlane(inc, 63);
   const int total = tot & 0xFFFF, nb_routed = tot >> 16;
   int run = inc - packed;
 #pragma unroll
