@@ -244,7 +244,7 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 // first group, 0 or 2).  frag(mt, g, h) is the address of this lane's 16
 // bytes of activations for row tile mt, group g of the step and half h (the
 // step's inputs 64 g + 32 h + 8 (lane / 16) .. +7 of row 16 mt + lane % 16).
-template <int SW, int MT, typename Frag>
+template <int SW, int MT, bool XIN = true, typename Frag>
 __device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const Frag& frag,
                                                 int wpos, int q4, const bf16x8& ones,
                                                 const PairConsts& pk, f32x4 (&acc)[MT][SW],
@@ -274,11 +274,13 @@ __device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const F
     for (int mt = 0; mt < MT; ++mt) {
       const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(frag(mt, g, 0));
       const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(frag(mt, g, 1));
-      f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a0, zero, 0, 0, 0);
-      X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a1, X, 0, 0, 0);
-      // the window's first group clears the other lanes' entries, so a step
-      // that is not computed contributes nothing
-      xk[mt] = (q4 == wg) ? X[0] : (wg == 0 ? 0.0f : xk[mt]);
+      if constexpr (XIN) {  // else the caller supplies xk (computed once per workgroup)
+        f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a0, zero, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a1, X, 0, 0, 0);
+        // the window's first group clears the other lanes' entries, so a step
+        // that is not computed contributes nothing
+        xk[mt] = (q4 == wg) ? X[0] : (wg == 0 ? 0.0f : xk[mt]);
+      }
 #pragma unroll
       for (int sl = 0; sl < SW; ++sl) {
         f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
@@ -337,8 +339,9 @@ template <int WAVES, int SW, bool GATE_UP, int MT>
 __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& bi,
                                             const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out,
-                                            uint16_t* As0, uint16_t* As1, int* s_tok) {
+                                            uint16_t* As0, uint16_t* As1, int* s_tok, float* Xw) {
   static_assert(MT == 1 || MT == 2, "16 or 32 rows");
+  static_assert(WAVES == 4, "each wave computes one (group, row tile) pair of the transposed X");
   const int K = GATE_UP ? a.H : a.I;
   const int nslices = GATE_UP ? a.I / 8 : a.H / 16;
   const int nk = pack_steps(K);
@@ -427,18 +430,36 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   // codes of step s+2 into the registers the products have read; then a wait
   // for the copies only (the codes stay in flight) and a barrier that does
   // not drain global loads.
+  // The transposed X of each (group, row tile) pair of a step is computed by
+  // one wave (wave w: group w mod 2, row tile (w / 2) mod MT) and shared
+  // through Xw[window parity][group of the window][row]; a step past the end
+  // stores zeros.  The window's reads follow the barrier of its second step,
+  // and the next writes to the same half come two steps later, after another
+  // barrier.
+  const int gx = wave & 1, mtx = (wave >> 1) % MT;
   auto step = [&](int s, SliceOps (&o)[SW], int buf) {
+    const uint16_t* tb = buf ? As1 : As0;
+    auto frag = [&](int mt, int g, int hh) {
+      const int r = mt * 16 + n;
+      return tb + r * kKS + (((q4 + 8 * g + 4 * hh) ^ n) << 3);
+    };
+    // X first: its LDS store then comes before the step's copies are issued,
+    // so it need not wait for them
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const bf16x8 ax0 = *reinterpret_cast<const bf16x8*>(frag(mtx, gx, 0));
+      const bf16x8 ax1 = *reinterpret_cast<const bf16x8*>(frag(mtx, gx, 1));
+      f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ax0, zero, 0, 0, 0);
+      X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ax1, X, 0, 0, 0);
+      if (lane < 16)
+        Xw[((s >> 1) & 1) * (4 * kSmallM) + (2 * buf + gx) * kSmallM + mtx * 16 + lane] =
+            s < nk ? X[0] : 0.0f;
+    }
     __builtin_amdgcn_sched_barrier(0);
     issue_a(s + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (active && s < nk) {
-      const uint16_t* tb = buf ? As1 : As0;
-      auto frag = [&](int mt, int g, int hh) {
-        const int r = mt * 16 + n;
-        return tb + r * kKS + (((q4 + 8 * g + 4 * hh) ^ n) << 3);
-      };
-      small_step_math<SW, MT>(o, frag, 2 * buf, q4, ones, pk, acc, xk, ck);
-    }
+    if (active && s < nk) small_step_math<SW, MT, false>(o, frag, 2 * buf, q4, ones, pk, acc, xk, ck);
     __builtin_amdgcn_sched_barrier(0);
     load_codes(s + 2, o);
     __builtin_amdgcn_sched_barrier(0);
@@ -460,6 +481,8 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
   do {  // nk >= 1: no guard in front of the loop, so no load sinks into it
     step(s, c0, 0);
     step(s + 1, c1, 1);  // past the end: loads clamped, no compute
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xk[mt] = Xw[((s >> 1) & 1) * (4 * kSmallM) + q4 * kSmallM + mt * 16 + n];
     small_window_bias<SW, MT>(acc, xk, ck);
     s += 2;
   } while (s < nk);
@@ -506,7 +529,7 @@ template <int WAVES, int SW, int MT, int DEPTH>
 __device__ __forceinline__ void down_resident_block(const GemmArgs& a, const BlockInfo& bi, int ntw,
                                                     const uint16_t* __restrict__ src,
                                                     uint16_t* __restrict__ out, uint16_t* As,
-                                                    uint16_t* Os) {
+                                                    uint16_t* Os, float* Xs) {
   constexpr int SPT = SW * WAVES;        // slices per N tile
   constexpr int TW = 16 * SPT;           // output columns per N tile
   constexpr int TP = TW + 8;             // output tile pitch (bf16)
@@ -569,6 +592,25 @@ __device__ __forceinline__ void down_resident_block(const GemmArgs& a, const Blo
   bf16x8 ones = bf16_ones();
   asm volatile("" : "+v"(ones));
   const PairConsts pk = pair_consts();
+  // X_g[m], the row sums of the resident rows over each group of 64 inputs,
+  // once per workgroup (the same two products per (row tile, group) that the
+  // small-tile step runs, so the same values), spread over the waves; every
+  // N tile and every wave then reads them from Xs[m][g]
+  constexpr int NG = kResK / 64;
+  {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const int ng = 2 * nk;
+    for (int p = wave; p < MT * ng; p += WAVES) {
+      const int mt = p / ng, g = p % ng;
+      const uint16_t* a0p = &As[(mt * 16 + n) * kResLDA + 64 * g + lk];
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(a0p);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(a0p + 32);
+      f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a0, zero, 0, 0, 0);
+      X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a1, X, 0, 0, 0);
+      if (lane < 16) Xs[(mt * 16 + lane) * NG + g] = X[0];
+    }
+  }
+  __syncthreads();
   f32x4 acc[MT][SW];
   float xk[MT], ck[SW];
   int f = 0;
@@ -588,10 +630,16 @@ __device__ __forceinline__ void down_resident_block(const GemmArgs& a, const Blo
         if (act && s + d < nk) {
           const uint16_t* ar = &As[n * kResLDA + (s + d) * kKS + lk];
           auto frag = [&](int mt, int g, int hh) { return ar + mt * 16 * kResLDA + 64 * g + 32 * hh; };
-          small_step_math<SW, MT>(cq[d], frag, 2 * (d & 1), q4, ones, pk, acc, xk, ck);
+          small_step_math<SW, MT, false>(cq[d], frag, 2 * (d & 1), q4, ones, pk, acc, xk, ck);
         }
         load_codes(f + d + DEPTH, cq[d]);
-        if (d & 1) small_window_bias<SW, MT>(acc, xk, ck);
+        if (d & 1) {
+          // this lane's group of the window: 4 window + q4 (steps past K: none)
+          const int g = 2 * (s + d - 1) + q4;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) xk[mt] = g < 2 * nk ? Xs[(mt * 16 + n) * NG + g] : 0.0f;
+          small_window_bias<SW, MT>(acc, xk, ck);
+        }
       }
     }
     // epilogue of tile t through one of two LDS tiles (the other may still be
@@ -618,14 +666,15 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3)))
     GemmArgs a, const uint16_t* __restrict__ src, uint16_t* __restrict__ out, int ntw) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kSmallM * kResLDA];
   __shared__ __attribute__((aligned(16))) uint16_t Os[2 * kSmallM * (16 * SW * WAVES + 8)];
+  __shared__ float Xs[kSmallM * (kResK / 64)];
   BlockInfo bi;
   if (!block_info<false>(a, bi, SW * WAVES * ntw)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<false>(a, bi, kSmallM)) return;
   if (bi.tm <= 16)
-    down_resident_block<WAVES, SW, 1, kResDepth>(a, bi, ntw, src, out, As, Os);
+    down_resident_block<WAVES, SW, 1, kResDepth>(a, bi, ntw, src, out, As, Os, Xs);
   else
-    down_resident_block<WAVES, SW, 2, kResDepth>(a, bi, ntw, src, out, As, Os);
+    down_resident_block<WAVES, SW, 2, kResDepth>(a, bi, ntw, src, out, As, Os, Xs);
 }
 
 // MODE: the blocks the launch computes (GemmArgs::shared_mode: 0 all, 1 the
@@ -640,15 +689,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ __attribute__((aligned(1024))) uint16_t As0[kSmallM * (kKS + 8)];
   __shared__ __attribute__((aligned(1024))) uint16_t As1[kSmallM * kKS];
   __shared__ int s_tok[kSmallM];
+  __shared__ float Xw[2 * 4 * kSmallM];
 
   BlockInfo bi;
   if (!block_info<GATE_UP>(a, bi, SW * WAVES)) return;
   if (bi.tm > kSmallM) return;  // a tall block: the tall-tile kernel owns it
   if (!block_valid<GATE_UP>(a, bi, kSmallM)) return;
   if (bi.tm <= 16)
-    small_block<WAVES, SW, GATE_UP, 1>(a, bi, src, out, As0, As1, s_tok);
+    small_block<WAVES, SW, GATE_UP, 1>(a, bi, src, out, As0, As1, s_tok, Xw);
   else
-    small_block<WAVES, SW, GATE_UP, 2>(a, bi, src, out, As0, As1, s_tok);
+    small_block<WAVES, SW, GATE_UP, 2>(a, bi, src, out, As0, As1, s_tok, Xw);
 }
 
 // ---------------------------------------------------------------------------
@@ -917,7 +967,7 @@ constexpr int kT4CT = 2;  // 32-column tiles per wave of the tall-tile kernel
 template <bool GATE_UP>
 __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ out, uint8_t* As0, uint8_t* As1,
-                                            int* s_tok) {
+                                            int* s_tok, float* Xw) {
   BlockInfo bi;
   if (!block_info<GATE_UP>(a, bi, 2 * kT4CT * kT4Waves)) return;
   if (bi.tm <= kSmallM && !a.tall_all) return;  // a short block: the small-tile kernel owns it
@@ -938,10 +988,10 @@ __device__ __forceinline__ void tall4_entry(const GemmArgs& a, const uint16_t* _
       if (p) __syncthreads();  // the first half's output tile has been stored
       if (half.tm <= 16)
         small_block<kSmallWaves, kSmallSlices, GATE_UP, 1>(a, half, src, out, reinterpret_cast<uint16_t*>(As0),
-                                                           reinterpret_cast<uint16_t*>(As1), s_tok);
+                                                           reinterpret_cast<uint16_t*>(As1), s_tok, Xw);
       else
         small_block<kSmallWaves, kSmallSlices, GATE_UP, 2>(a, half, src, out, reinterpret_cast<uint16_t*>(As0),
-                                                           reinterpret_cast<uint16_t*>(As1), s_tok);
+                                                           reinterpret_cast<uint16_t*>(As1), s_tok, Xw);
     }
     return;
   }
@@ -959,7 +1009,8 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
   __shared__ int s_tok[kTallM];
-  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
+  __shared__ float Xw[2 * 4 * kSmallM];
+  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok, Xw);
 }
 
 // The same kernel for the launches that compute only the routed blocks and only
@@ -971,7 +1022,8 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
   __shared__ int s_tok[kTallM];
-  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
+  __shared__ float Xw[2 * 4 * kSmallM];
+  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok, Xw);
 }
 
 template <bool GATE_UP>
@@ -980,7 +1032,8 @@ __global__ __launch_bounds__(kT4Threads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ __attribute__((aligned(1024))) uint8_t As0[kTallBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[kTallBuf];
   __shared__ int s_tok[kTallM];
-  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok);
+  __shared__ float Xw[2 * 4 * kSmallM];
+  tall4_entry<GATE_UP>(a, src, out, As0, As1, s_tok, Xw);
 }
 
 // ---------------------------------------------------------------------------
