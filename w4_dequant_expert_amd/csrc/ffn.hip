@@ -234,7 +234,10 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 // keeps group 4w + q.  X comes from the matrix core transposed (ones times
 // the activation fragment, so lane l receives X_g[l mod 16]), which is
 // already the A layout of the float32 MFMA; c[n][g] is the lane's own
-// column's.  Two steps make one window.
+// column's.  Two steps make one window.  X depends only on the activations:
+// one wave forms each (group, row tile) pair and the others read it from LDS
+// (small_block), or the whole block's X is formed once (the resident-
+// activation down kernel); small_step_math<..., true> forms it in every wave.
 // ---------------------------------------------------------------------------
 
 // One step of the small-tile product for SW slices and MT row tiles: the
