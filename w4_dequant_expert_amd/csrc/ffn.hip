@@ -237,21 +237,22 @@ __device__ __forceinline__ void block_tokens(const GemmArgs& a, const BlockInfo&
 // column's.  Two steps make one window.  X depends only on the activations:
 // one wave forms each (group, row tile) pair and the others read it from LDS
 // (small_block), or the whole block's X is formed once (the resident-
-// activation down kernel); small_step_math<..., true> forms it in every wave.
+// activation down kernel).
 // ---------------------------------------------------------------------------
 
 // One step of the small-tile product for SW slices and MT row tiles: the
-// slices' 128 + q operands, per tile and group the transposed X and the P of
-// each slice on the matrix core, P s into the accumulators and this lane's X
-// and c for its group of the window (wpos: the window place of the step's
-// first group, 0 or 2).  frag(mt, g, h) is the address of this lane's 16
-// bytes of activations for row tile mt, group g of the step and half h (the
-// step's inputs 64 g + 32 h + 8 (lane / 16) .. +7 of row 16 mt + lane % 16).
-template <int SW, int MT, bool XIN = true, typename Frag>
+// slices' 128 + q operands, per tile and group the P of each slice on the
+// matrix core, P s into the accumulators and this lane's c for its group of
+// the window (wpos: the window place of the step's first group, 0 or 2; the
+// window's first group clears the other lanes' entries, so a step that is not
+// computed contributes nothing).  The window's X comes from the caller.
+// frag(mt, g, h) is the address of this lane's 16 bytes of activations for
+// row tile mt, group g of the step and half h (the step's inputs
+// 64 g + 32 h + 8 (lane / 16) .. +7 of row 16 mt + lane % 16).
+template <int SW, int MT, typename Frag>
 __device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const Frag& frag,
-                                                int wpos, int q4, const bf16x8& ones,
-                                                const PairConsts& pk, f32x4 (&acc)[MT][SW],
-                                                float (&xk)[MT], float (&ck)[SW]) {
+                                                int wpos, int q4, const PairConsts& pk,
+                                                f32x4 (&acc)[MT][SW], float (&ck)[SW]) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   uint32_t qw[SW][4];
   float gs[SW][2], gc[SW][2];
@@ -277,13 +278,6 @@ __device__ __forceinline__ void small_step_math(const SliceOps (&o)[SW], const F
     for (int mt = 0; mt < MT; ++mt) {
       const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(frag(mt, g, 0));
       const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(frag(mt, g, 1));
-      if constexpr (XIN) {  // else the caller supplies xk (computed once per workgroup)
-        f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a0, zero, 0, 0, 0);
-        X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, a1, X, 0, 0, 0);
-        // the window's first group clears the other lanes' entries, so a step
-        // that is not computed contributes nothing
-        xk[mt] = (q4 == wg) ? X[0] : (wg == 0 ? 0.0f : xk[mt]);
-      }
 #pragma unroll
       for (int sl = 0; sl < SW; ++sl) {
         f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq[sl][0], zero, 0, 0, 0);
@@ -462,7 +456,7 @@ __device__ __forceinline__ void small_block(const GemmArgs& a, const BlockInfo& 
     __builtin_amdgcn_sched_barrier(0);
     issue_a(s + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (active && s < nk) small_step_math<SW, MT, false>(o, frag, 2 * buf, q4, ones, pk, acc, xk, ck);
+    if (active && s < nk) small_step_math<SW, MT>(o, frag, 2 * buf, q4, pk, acc, ck);
     __builtin_amdgcn_sched_barrier(0);
     load_codes(s + 2, o);
     __builtin_amdgcn_sched_barrier(0);
@@ -633,7 +627,7 @@ __device__ __forceinline__ void down_resident_block(const GemmArgs& a, const Blo
         if (act && s + d < nk) {
           const uint16_t* ar = &As[n * kResLDA + (s + d) * kKS + lk];
           auto frag = [&](int mt, int g, int hh) { return ar + mt * 16 * kResLDA + 64 * g + 32 * hh; };
-          small_step_math<SW, MT, false>(cq[d], frag, 2 * (d & 1), q4, ones, pk, acc, xk, ck);
+          small_step_math<SW, MT>(cq[d], frag, 2 * (d & 1), q4, pk, acc, ck);
         }
         load_codes(f + d + DEPTH, cq[d]);
         if (d & 1) {
